@@ -1,0 +1,203 @@
+"""Benchmark: causal attention forward + backward on one MI355X.
+
+One step = one pass of the whole path over one batch of the synthetic
+long-context workload (B4, S2048, 16 heads of 64, bf16 in / fp32 accumulate):
+xattn_fwd, then the backward as its two kernels (xattn_bwd_dq, xattn_bwd_dkdv,
+which together are exactly xattn_bwd), all through the C ABI on torch's current
+stream with inputs resident in HBM.  W untimed warmup steps, then K timed steps
+between synchronisations.  HIP events between the kernels give each kernel's
+average duration inside the timed region; the dominant kernel's roofline is
+reported against MI355X's dense bf16 MFMA peak.
+
+Counted FLOPs (the FlashAttention-2 convention, causal half only):
+    fwd 4*hd*nnz, bwd 10*hd*nnz per (batch, head), nnz = S(S+1)/2
+Per-kernel algorithmic FLOPs per (batch, head): fwd 4*hd*nnz (Q.K^T, P.V),
+dq kernel 6*hd*nnz (S, dP, dS.K), dk/dv kernel 8*hd*nnz (S, dP, P^T.dO, dS^T.Q).
+
+The CPU baseline times the fp64 oracle on a bounded sample of the same
+workload (whole (batch, kv head) units) on the host's cores, rank 0, N = 1.
+
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s & % MFMA peak (B16 S256 H12 hd32; B4 S2048 hd64)"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+HBM_GBS = 8000.0
+
+
+def counted_flops(w):
+    nnz = w.S * (w.S + 1) / 2
+    per = w.B * w.H * nnz * w.hd
+    return {"fwd": 4 * per, "bwd": 10 * per, "total": 14 * per,
+            "k_fwd": 4 * per, "k_dq": 6 * per, "k_dkdv": 8 * per}
+
+
+def run_gpu(w, steps, warmup):
+    import numpy as np
+    import torch
+
+    from bwd_head_rms_amd import _lib, inputs
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    arrs = inputs.generate_workload(w)
+    t = {n: inputs.to_torch(a, w.dtype, dev) for n, a in arrs.items()}
+    code = _lib.BF16 if w.dtype == "bf16" else _lib.F32
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty(t["q"].shape, **f32)
+    dk = torch.empty(t["k"].shape, **f32)
+    dv = torch.empty(t["k"].shape, **f32)
+    ws_bytes = int(L.xattn_bwd_workspace_bytes(w.B, w.S, w.H, w.Hkv, w.hd, code))
+    ws = torch.empty(ws_bytes // 4, **f32)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    dims = (w.B, w.S, w.H, w.Hkv, w.hd, w.scale, code)
+    p = {n: x.data_ptr() for n, x in dict(q=t["q"], k=t["k"], v=t["v"], dO=t["dO"], o=o, lse=lse,
+                                          dq=dq, dk=dk, dv=dv, ws=ws).items()}
+
+    def fwd():
+        _lib.check(L.xattn_fwd(p["q"], p["k"], p["v"], p["o"], p["lse"], *dims, sh))
+
+    def bwd_dq():
+        _lib.check(L.xattn_bwd_dq(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"],
+                                  *dims, p["ws"], ws_bytes, sh))
+
+    def bwd_dkdv():
+        _lib.check(L.xattn_bwd_dkdv(p["q"], p["k"], p["v"], p["lse"], p["dO"], p["dk"], p["dv"],
+                                    *dims, p["ws"], ws_bytes, sh))
+
+    for _ in range(warmup):
+        fwd(); bwd_dq(); bwd_dkdv()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd_dq()
+        ev[i][2].record(stream)
+        bwd_dkdv()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev[0][0].elapsed_time(ev[-1][3])
+    per = {"fwd": [], "dq": [], "dkdv": []}
+    for e in ev:
+        per["fwd"].append(e[0].elapsed_time(e[1]))
+        per["dq"].append(e[1].elapsed_time(e[2]))
+        per["dkdv"].append(e[2].elapsed_time(e[3]))
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    return {"ms_per_step": total_ms / steps, "wall_s": wall, "kernel_ms": avg,
+            "device": torch.cuda.get_device_name(dev)}
+
+
+def cpu_baseline(w, budget_units=None):
+    """Time the fp64 oracle on whole (batch, kv head) units of the workload."""
+    import numpy as np
+
+    from bwd_head_rms_amd import inputs
+    from oracle import default
+
+    ref = default()
+    threads = ref.max_threads()
+    n_units = budget_units or max(1, min(w.B * w.Hkv, 2 * threads))
+    arrs = inputs.generate_workload(w)
+    b_needed = (n_units + w.Hkv - 1) // w.Hkv
+    sub = {n: np.ascontiguousarray(a[:b_needed]) for n, a in arrs.items()}
+    t0 = time.perf_counter()
+    ref.run(sub["q"], sub["k"], sub["v"], sub["dO"], scale=w.scale, units=(0, n_units))
+    dt = time.perf_counter() - t0
+    nnz = w.S * (w.S + 1) / 2
+    flops = 14 * nnz * w.hd * n_units * (w.H // w.Hkv)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": dt,
+            "sample": f"{n_units} of {w.B * w.Hkv} (batch, kv head) units of {w.name} "
+                      f"({n_units * (w.H // w.Hkv)} heads x S={w.S}, fwd+bwd, fp64)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="name from bwd_head_rms_amd.inputs.WORKLOADS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by batch or kv-head group with no exchange inside attention).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from bwd_head_rms_amd import inputs
+    w = inputs.WORKLOADS[args.workload or inputs.LONG_CONTEXT]
+    fl = counted_flops(w)
+    r = run_gpu(w, args.steps, args.warmup)
+    sec = r["ms_per_step"] / 1e3
+    tflops = fl["total"] / sec / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    km = r["kernel_ms"]
+    kflops = {"fwd": fl["k_fwd"], "dq": fl["k_dq"], "dkdv": fl["k_dkdv"]}
+    dom = max(km, key=km.get)
+    ach = kflops[dom] / (km[dom] / 1e3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "Hkv": w.Hkv, "hd": w.hd,
+                   "scale": w.scale, "causal": True, "parallelism": "none (1 GPU)"},
+        "pct_of_mfma_peak": round(100 * tflops / peak, 3),
+        "tokens_per_s": round(w.B * w.S / sec, 1),
+        "fwd_tflops": round(fl["fwd"] / (km["fwd"] / 1e3) / 1e12, 3),
+        "bwd_tflops": round(fl["bwd"] / ((km["dq"] + km["dkdv"]) / 1e3) / 1e12, 3),
+        "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in km.items()},
+        "roofline": {"bound": "mfma", "kernel": {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel",
+                                                   "dkdv": "attn_bwd_dkdv_kernel"}[dom],
+                     "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ach / peak, 5), "traffic": None},
+        "device": r["device"],
+    }
+    if not args.no_secondary and args.workload is None:
+        w2 = inputs.WORKLOADS["dim384_b16_s256_h12_hd32_f32"]
+        r2 = run_gpu(w2, args.steps, args.warmup)
+        s2 = r2["ms_per_step"] / 1e3
+        t2 = counted_flops(w2)["total"] / s2 / 1e12
+        out["secondary"] = {"workload": w2.name, "dtype": w2.dtype, "tflops": round(t2, 3),
+                            "pct_of_mfma_peak": round(100 * t2 / PEAK_TFLOPS[w2.dtype], 3),
+                            "ms_per_step": round(r2["ms_per_step"], 5),
+                            "tokens_per_s": round(w2.B * w2.S / s2, 1),
+                            "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in r2["kernel_ms"].items()}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,113 @@
+"""PyTorch-facing binding of the causal attention library.
+
+Argument marshalling only: tensors are checked and their device pointers and
+the current HIP stream are handed to the C ABI; every arithmetic step runs in
+the HIP kernels of libxattn.so.  PyTorch provides device memory and streams.
+"""
+import math
+
+import torch
+
+from ._lib import BF16, F32, XattnError, check, lib
+
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _code(t):
+    if t.dtype not in _DTYPES:
+        raise XattnError(5, f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _check_tensor(t, name, shape, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise XattnError(1, f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise XattnError(2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise XattnError(5, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise XattnError(2, f"{name} must be contiguous (BHSD)")
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise XattnError(2, "q and k must be 4-D [B, heads, S, hd]")
+    B, H, S, hd = q.shape
+    Hkv = k.shape[1]
+    return B, S, H, Hkv, hd
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def fwd(q, k, v, scale=None, o=None, lse=None):
+    """Causal attention forward.  q [B,H,S,hd]; k, v [B,Hkv,S,hd] (fp32 or bf16).
+
+    Returns (o [B,H,S,hd] in the input dtype, lse [B,H,S] fp32).
+    """
+    B, S, H, Hkv, hd = _dims(q, k)
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check_tensor(q, "q", (B, H, S, hd), q.dtype)
+    _check_tensor(k, "k", (B, Hkv, S, hd), q.dtype)
+    _check_tensor(v, "v", (B, Hkv, S, hd), q.dtype)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor(o, "o", (B, H, S, hd), q.dtype)
+    _check_tensor(lse, "lse", (B, H, S), torch.float32)
+    check(lib().xattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, S, H, Hkv, hd, scale, _code(q), _stream(q)))
+    return o, lse
+
+
+def workspace_bytes(B, S, H, Hkv, hd, dtype_code):
+    return int(lib().xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype_code))
+
+
+def bwd(q, k, v, o, lse, dO, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Causal attention backward.  Returns fp32 (dq [B,H,S,hd], dk, dv [B,Hkv,S,hd])."""
+    B, S, H, Hkv, hd = _dims(q, k)
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    dt = q.dtype
+    for t, n, shp in ((q, "q", (B, H, S, hd)), (k, "k", (B, Hkv, S, hd)), (v, "v", (B, Hkv, S, hd)),
+                      (o, "o", (B, H, S, hd)), (dO, "dO", (B, H, S, hd))):
+        _check_tensor(t, n, shp, dt)
+    _check_tensor(lse, "lse", (B, H, S), torch.float32)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty((B, H, S, hd), **f32) if dq is None else dq
+    dk = torch.empty((B, Hkv, S, hd), **f32) if dk is None else dk
+    dv = torch.empty((B, Hkv, S, hd), **f32) if dv is None else dv
+    _check_tensor(dq, "dq", (B, H, S, hd), torch.float32)
+    _check_tensor(dk, "dk", (B, Hkv, S, hd), torch.float32)
+    _check_tensor(dv, "dv", (B, Hkv, S, hd), torch.float32)
+    need = workspace_bytes(B, S, H, Hkv, hd, _code(q))
+    if workspace is None:
+        workspace = torch.empty((max(1, need // 4),), **f32)
+    check(lib().xattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          dO.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          B, S, H, Hkv, hd, scale, _code(q),
+                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                          _stream(q)))
+    return dq, dk, dv
+
+
+class CausalAttention(torch.autograd.Function):
+    """autograd wrapper: o = causal_attention(q, k, v); grads are fp32 cast to the input dtype."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale=None):
+        o, lse = fwd(q, k, v, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, dO):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, dO.contiguous().to(q.dtype), ctx.scale)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None
+
+
+def causal_attention(q, k, v, scale=None):
+    return CausalAttention.apply(q, k, v, scale)

@@ -1,0 +1,136 @@
+// api.cpp -- the C ABI of libxattn.so (declared in include/xattn.h).
+//
+// Every argument is checked here, on the host, before any HIP call; only a
+// fully valid call enqueues kernels.  The library holds no state: no handles,
+// no allocations, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "launch.hpp"
+#include "xattn.h"
+
+namespace {
+
+constexpr int kTileRows = 128;  // rows per workgroup in every kernel (4 waves x 32)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int S, int H, int Hkv, int hd) {
+  if (B <= 0 || S <= 0 || H <= 0 || Hkv <= 0 || hd <= 0) return XATTN_ERR_SHAPE;
+  if (H % Hkv != 0) return XATTN_ERR_GQA;
+  if (hd != 16 && hd != 32 && hd != 64) return XATTN_ERR_HEAD_DIM;
+  const int64_t plane = (int64_t)S * hd;  // elements of one (batch, head) plane
+  if (plane > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
+  const int64_t tiles = ((int64_t)S + kTileRows - 1) / kTileRows;
+  if (tiles * B * H > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
+  if ((int64_t)B * H * S > std::numeric_limits<int64_t>::max() / 8) return XATTN_ERR_SHAPE;
+  return XATTN_OK;
+}
+
+int check_common(int B, int S, int H, int Hkv, int hd, float scale, int dtype) {
+  if (dtype != XATTN_F32 && dtype != XATTN_BF16) return XATTN_ERR_DTYPE;
+  const int rc = check_shape(B, S, H, Hkv, hd);
+  if (rc != XATTN_OK) return rc;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return XATTN_ERR_SCALE;
+  return XATTN_OK;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? XATTN_OK : XATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S,
+              int H, int Hkv, int hd, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return XATTN_ERR_NULL;
+  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_fwd(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, o, lse, scale,
+                    static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype) {
+  if (dtype != XATTN_F32 && dtype != XATTN_BF16) return 0;
+  if (check_shape(B, S, H, Hkv, hd) != XATTN_OK) return 0;
+  return sizeof(float) * (size_t)B * (size_t)H * (size_t)S;
+}
+
+int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dO, float* dq, int B, int S, int H, int Hkv, int hd, float scale,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq) return XATTN_ERR_NULL;
+  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!workspace || workspace_bytes < xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype))
+    return XATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dq) || !aligned16(workspace))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_bwd_dq(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, o, lse, dO, dq,
+                       static_cast<float*>(workspace), scale, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                   const void* dO, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
+                   float scale, int dtype, const void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!q || !k || !v || !lse || !dO || !dk || !dv) return XATTN_ERR_NULL;
+  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!workspace || workspace_bytes < xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype))
+    return XATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dO) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_bwd_dkdv(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, lse, dO,
+                         static_cast<const float*>(workspace), dk, dv, scale,
+                         static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, float* dq, float* dk, float* dv, int B, int S, int H, int Hkv,
+              int hd, float scale, int dtype, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  // Validate everything up front so that an invalid call enqueues nothing.
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return XATTN_ERR_NULL;
+  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!workspace || workspace_bytes < xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype))
+    return XATTN_ERR_WORKSPACE;
+  if (!aligned16(dk) || !aligned16(dv)) return XATTN_ERR_ALIGN;
+  rc = xattn_bwd_dq(q, k, v, o, lse, dO, dq, B, S, H, Hkv, hd, scale, dtype, workspace,
+                    workspace_bytes, stream);
+  if (rc != XATTN_OK) return rc;
+  return xattn_bwd_dkdv(q, k, v, lse, dO, dk, dv, B, S, H, Hkv, hd, scale, dtype, workspace,
+                        workspace_bytes, stream);
+}
+
+const char* xattn_strerror(int status) {
+  switch (status) {
+    case XATTN_OK: return "success";
+    case XATTN_ERR_NULL: return "a required pointer is NULL";
+    case XATTN_ERR_SHAPE: return "invalid shape: B, S, H, Hkv and hd must be positive and within size limits";
+    case XATTN_ERR_GQA: return "H must be a multiple of Hkv";
+    case XATTN_ERR_HEAD_DIM: return "head dimension must be 16, 32 or 64";
+    case XATTN_ERR_DTYPE: return "dtype must be XATTN_F32 or XATTN_BF16";
+    case XATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than xattn_bwd_workspace_bytes()";
+    case XATTN_ERR_SCALE: return "scale must be positive and finite";
+    case XATTN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case XATTN_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    default: return "unknown xattn status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+// attn_bwd_dkdv.hip -- causal attention backward, key/value side, for gfx950.
+//
+// One workgroup (4 waves) per (batch, kv head, 128-row key tile); each wave owns
+// 32 key rows whose K and V operands stay in registers for the whole kernel.
+// The workgroup walks every query head of its GQA group (r ascending) and, for
+// each, the 64-row query tiles at or below the diagonal (ascending), staging Q,
+// dO (row-major, plus transposed copies for bf16), LSE and D through LDS with
+// register prefetch.  Per 32-row query block and wave:
+//   S  = Q . K^T,   P = exp2(S*scale*log2e - LSE_i*log2e)     (recompute)
+//   dP = dO . V^T,  dS = P * (dP - D_i)
+//   dV^T += dO^T . P          (P feeds the product from registers)
+//   dK^T += Q^T . dS
+// dk = scale * dK and dv are written in fp32 once.  The GQA group sum happens in
+// registers in a fixed order (head r, then query tile), with no atomics, so the
+// result is bitwise reproducible (the deterministic group sum of the
+// "xtrain evolution overview", infra table row T15).  D comes from the dq
+// kernel, which runs first on the same stream.  Work order: heaviest key tiles
+// (those near the start of the sequence) first.
+#include "attn_device.hpp"
+#include "launch.hpp"
+
+namespace xattn {
+
+template <typename T, int HD>
+struct DkvCfg {
+  static constexpr int NW = 4, NT = NW * kWave, BN = 32 * NW, BMQ = 64, NQB = BMQ / 32;
+  static constexpr int RS = HD + Mma<T>::PADR;
+  static constexpr int TS = BMQ + 4;
+  static constexpr int ND = HD >= 32 ? HD / 32 : 1;
+  static constexpr int NKS = HD / Mma<T>::KSTEP;
+  static constexpr int NAS = 32 / Mma<T>::KSTEP;
+  static constexpr bool TR = sizeof(T) == 2;  // bf16 keeps Q and dO transposed too
+  static constexpr int R_ELEMS = BMQ * RS;
+  static constexpr int T_ELEMS = TR ? HD * TS : 8;
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ dws,
+    float* __restrict__ dk, float* __restrict__ dv, int S, int H, int Hkv, int nkt, int BG,
+    float c, float scale) {
+  using C = DkvCfg<T, HD>;
+  using M = Mma<T>;
+  __shared__ __align__(16) T sQ[C::R_ELEMS];
+  __shared__ __align__(16) T sQt[C::T_ELEMS];
+  __shared__ __align__(16) T sO[C::R_ELEMS];   // dO, row-major
+  __shared__ __align__(16) T sOt[C::T_ELEMS];  // dO, transposed (bf16)
+  __shared__ float sL[C::BMQ];                 // LSE * log2e
+  __shared__ float sD[C::BMQ];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int li = lane & 31, g = lane >> 5;
+  const int bid = blockIdx.x;
+  const int kt = bid / BG;  // key tile 0 (the heaviest) first
+  const int bg = bid % BG;
+  const int b = bg / Hkv, kvh = bg % Hkv;
+  const int group = H / Hkv;
+  const size_t kvplane = ((size_t)b * Hkv + kvh) * S * HD;
+
+  const int kv0 = kt * C::BN + wave * 32;
+  const int my_kv = kv0 + li;
+  const bool kv_ok = my_kv < S;
+  const bool wave_live = kv0 < S;
+
+  typename M::frag kf[C::NKS], vf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    kf[ks] = kv_ok ? row_frag_global<T, HD>(k + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
+    vf[ks] = kv_ok ? row_frag_global<T, HD>(v + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
+  }
+
+  f32x16 dkacc[C::ND], dvacc[C::ND];
+#pragma unroll
+  for (int d = 0; d < C::ND; ++d) {
+    dkacc[d] = zero_acc();
+    dvacc[d] = zero_acc();
+  }
+
+  const int qt_first = (kt * C::BN) / C::BMQ;
+  const int nq = (S + C::BMQ - 1) / C::BMQ;
+  const int per_head = nq - qt_first;
+  const int iters = group * per_head;
+
+  TileStage<T, HD, C::BMQ, C::NT, true, C::TR> stQ, stO;
+  float pre_l = 0.f, pre_d = 0.f;
+  auto prefetch = [&](int it) {
+    const int r = it / per_head, qt = qt_first + it % per_head;
+    const size_t bh = (size_t)b * H + (size_t)kvh * group + r;
+    const int row0 = qt * C::BMQ;
+    stQ.load(q + bh * S * HD, row0, S - row0, tid);
+    stO.load(dO + bh * S * HD, row0, S - row0, tid);
+    if (tid < C::BMQ) {
+      const int qi = row0 + tid;
+      pre_l = qi < S ? lse[bh * S + qi] * kLog2e : 0.f;
+      pre_d = qi < S ? dws[bh * S + qi] : 0.f;
+    }
+  };
+  if (iters > 0) prefetch(0);
+
+  for (int it = 0; it < iters; ++it) {
+    const int qt = qt_first + it % per_head;
+    __syncthreads();
+    stQ.template store<C::RS, C::TS>(sQ, sQt, tid);
+    stO.template store<C::RS, C::TS>(sO, sOt, tid);
+    if (tid < C::BMQ) {
+      sL[tid] = pre_l;
+      sD[tid] = pre_d;
+    }
+    __syncthreads();
+    if (it + 1 < iters) prefetch(it + 1);
+    if (!wave_live) continue;
+
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      const int qb0 = qt * C::BMQ + 32 * qb;
+      if (qb0 + 31 < kv0 || qb0 >= S) continue;  // wholly above the diagonal, or past S
+      const bool need_mask = (kv0 + 31 > qb0) || (qb0 + 32 > S);
+      f32x16 s = zero_acc(), dp = zero_acc();
+      const T* qrow = sQ + (32 * qb + li) * C::RS;
+      const T* orow = sO + (32 * qb + li) * C::RS;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        M::mma(s, row_frag_lds<T, HD>(qrow, g, ks), kf[ks]);
+        M::mma(dp, row_frag_lds<T, HD>(orow, g, ks), vf[ks]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = 32 * qb + acc_row(r, g);
+        float p = fast_exp2(fmaf(s[r], c, -sL[ql]));
+        if (need_mask) {
+          const int qi = qt * C::BMQ + ql;
+          if (my_kv > qi || qi >= S) p = 0.f;
+        }
+        s[r] = p;
+        dp[r] = p * (dp[r] - sD[ql]);  // dS
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::NAS; ++ks) {
+        const typename M::frag pf = acc_frag<T>(s, ks * M::KPL);
+        const typename M::frag sf = acc_frag<T>(dp, ks * M::KPL);
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db) {
+          const int d = min(32 * db + li, HD - 1);
+          typename M::frag ao, aq;
+          if constexpr (C::TR) {
+            ao = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sOt) + d * C::TS + 32 * qb, g, ks);
+            aq = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sQt) + d * C::TS + 32 * qb, g, ks);
+          } else {
+            ao = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sO) + 32 * qb * C::RS, d, g, ks);
+            aq = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sQ) + 32 * qb * C::RS, d, g, ks);
+          }
+          M::mma(dvacc[db], ao, pf);
+          M::mma(dkacc[db], aq, sf);
+        }
+      }
+    }
+  }
+
+  if (!wave_live || !kv_ok) return;
+  float* krow = dk + kvplane + (size_t)my_kv * HD;
+  float* vrow = dv + kvplane + (size_t)my_kv * HD;
+#pragma unroll
+  for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * db + 8 * rg + 4 * g;
+      if (d0 < HD) {
+        store4<float>(krow + d0, scale * dkacc[db][4 * rg], scale * dkacc[db][4 * rg + 1],
+                      scale * dkacc[db][4 * rg + 2], scale * dkacc[db][4 * rg + 3]);
+        store4<float>(vrow + d0, dvacc[db][4 * rg], dvacc[db][4 * rg + 1], dvacc[db][4 * rg + 2],
+                      dvacc[db][4 * rg + 3]);
+      }
+    }
+}
+
+template <typename T, int HD>
+static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* v,
+                       const float* lse, const void* dO, const float* dws, float* dk, float* dv,
+                       float scale, hipStream_t stream) {
+  using C = DkvCfg<T, HD>;
+  const int nkt = (d.S + C::BN - 1) / C::BN;
+  const int BG = d.B * d.Hkv;
+  dim3 grid((unsigned)(nkt * BG)), block(C::NT);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
+                     (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, d.S, d.H, d.Hkv,
+                     nkt, BG, scale * kLog2e, scale);
+}
+
+void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,
+                     const float* lse, const void* dO, const float* dws, float* dk, float* dv,
+                     float scale, hipStream_t stream) {
+  if (dtype == 0) {
+    if (d.hd == 16) dkdv_typed<float, 16>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+    else if (d.hd == 32) dkdv_typed<float, 32>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+    else dkdv_typed<float, 64>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+  } else {
+    if (d.hd == 16) dkdv_typed<bf16, 16>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+    else if (d.hd == 32) dkdv_typed<bf16, 32>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+    else dkdv_typed<bf16, 64>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+  }
+}
+
+}  // namespace xattn

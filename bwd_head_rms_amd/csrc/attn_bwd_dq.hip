@@ -1,0 +1,189 @@
+// attn_bwd_dq.hip -- causal attention backward, query side, for gfx950.
+//
+// One workgroup (4 waves) per (batch, head, 128-row query tile); each wave owns
+// 32 query rows, as in the forward.  The prologue computes
+//   D_i = sum_d dO_id * o_id
+// (the simplification of the softmax Jacobian in the fused kernel of the
+// "xtrain evolution overview", infra table row T14) and stores it for the
+// dK/dV kernel.  Then, over the key tiles j <= i:
+//   S^T  = K . Q^T,   P^T = exp2(S^T*scale*log2e - LSE_i*log2e)   (recompute)
+//   dP^T = V . dO^T
+//   dS^T = P^T * (dP^T - D_i)
+//   dQ^T += K^T . dS^T          (dS feeds the product from registers)
+// and dq = scale * dQ is written in fp32.  K, K^T (bf16 only) and V tiles are
+// staged through LDS with register prefetch; query head h reads kv head
+// h / (H / Hkv) by address.
+#include "attn_device.hpp"
+#include "launch.hpp"
+
+namespace xattn {
+
+template <typename T, int HD>
+struct DqCfg {
+  static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
+  static constexpr int RS = HD + Mma<T>::PADR;
+  static constexpr int TS = BN + 4;
+  static constexpr int ND = HD >= 32 ? HD / 32 : 1;
+  static constexpr int NKS = HD / Mma<T>::KSTEP;
+  static constexpr int NAS = 32 / Mma<T>::KSTEP;
+  static constexpr bool KT = sizeof(T) == 2;  // bf16 also keeps K transposed in LDS
+  static constexpr int K_ELEMS = BN * RS;
+  static constexpr int KT_ELEMS = KT ? HD * TS : 8;
+  static constexpr int V_ELEMS = BN * RS;
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ o, const float* __restrict__ lse, const T* __restrict__ dO,
+    float* __restrict__ dq, float* __restrict__ dws, int S, int H, int Hkv, int nqt, int BH,
+    float c, float scale) {
+  using C = DqCfg<T, HD>;
+  using M = Mma<T>;
+  __shared__ __align__(16) T sK[C::K_ELEMS];
+  __shared__ __align__(16) T sKt[C::KT_ELEMS];
+  __shared__ __align__(16) T sV[C::V_ELEMS];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int li = lane & 31, g = lane >> 5;
+  const int bid = blockIdx.x;
+  const int qt = nqt - 1 - bid / BH;
+  const int bh = bid % BH;
+  const int b = bh / H, h = bh % H;
+  const int kvh = h / (H / Hkv);
+  const size_t qplane = (size_t)bh * S * HD;
+  const T* kp = k + ((size_t)b * Hkv + kvh) * S * HD;
+  const T* vp = v + ((size_t)b * Hkv + kvh) * S * HD;
+
+  const int q0 = qt * C::BM + wave * 32;
+  const int my_q = q0 + li;
+  const bool q_ok = my_q < S;
+  const bool wave_live = q0 < S;
+  const int wave_kv_end = min(S, q0 + 32);
+
+  typename M::frag qf[C::NKS], df[C::NKS];
+  float Dp = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    if (q_ok) {
+      qf[ks] = row_frag_global<T, HD>(q + qplane + (size_t)my_q * HD, g, ks);
+      df[ks] = row_frag_global<T, HD>(dO + qplane + (size_t)my_q * HD, g, ks);
+      const typename M::frag of = row_frag_global<T, HD>(o + qplane + (size_t)my_q * HD, g, ks);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) Dp += (float)of[t] * (float)df[ks][t];
+      } else {
+        Dp += of * df[ks];
+      }
+    } else {
+      qf[ks] = zero_frag<T>();
+      df[ks] = zero_frag<T>();
+    }
+  }
+  const float Drow = Dp + __shfl_xor(Dp, 32);
+  if (q_ok && g == 0) dws[(size_t)bh * S + my_q] = Drow;
+  const float lse2 = q_ok ? lse[(size_t)bh * S + my_q] * kLog2e : 0.f;
+
+  f32x16 acc[C::ND];
+#pragma unroll
+  for (int d = 0; d < C::ND; ++d) acc[d] = zero_acc();
+
+  const int kv_end = min(S, qt * C::BM + C::BM);
+  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+
+  TileStage<T, HD, C::BN, C::NT, true, C::KT> stK;
+  TileStage<T, HD, C::BN, C::NT, true, false> stV;
+  stK.load(kp, 0, S, tid);
+  stV.load(vp, 0, S, tid);
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv_t0 = j * C::BN;
+    __syncthreads();
+    stK.template store<C::RS, C::TS>(sK, sKt, tid);
+    stV.template store<C::RS, C::TS>(sV, nullptr, tid);
+    __syncthreads();
+    if (j + 1 < ntiles) {
+      stK.load(kp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
+      stV.load(vp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
+    }
+    if (!wave_live || kv_t0 >= wave_kv_end) continue;
+    const bool need_mask = (kv_t0 + C::BN - 1 > q0) || (kv_t0 + C::BN > S);
+
+#pragma unroll
+    for (int cb = 0; cb < C::NB; ++cb) {
+      if (kv_t0 + 32 * cb >= wave_kv_end) continue;
+      f32x16 s = zero_acc(), dp = zero_acc();
+      const T* krow = sK + (32 * cb + li) * C::RS;
+      const T* vrow = sV + (32 * cb + li) * C::RS;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        M::mma(s, row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
+        M::mma(dp, row_frag_lds<T, HD>(vrow, g, ks), df[ks]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[r], c, -lse2));
+        if (need_mask) {
+          const int kv = kv_t0 + 32 * cb + acc_row(r, g);
+          if (kv > my_q || kv >= S) p = 0.f;
+        }
+        s[r] = p * (dp[r] - Drow);  // dS^T
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::NAS; ++ks) {
+        const typename M::frag sf = acc_frag<T>(s, ks * M::KPL);
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db) {
+          const int d = min(32 * db + li, HD - 1);
+          typename M::frag a;
+          if constexpr (C::KT)
+            a = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sKt) + d * C::TS + 32 * cb, g, ks);
+          else
+            a = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sK) + 32 * cb * C::RS, d, g, ks);
+          M::mma(acc[db], a, sf);
+        }
+      }
+    }
+  }
+
+  if (!wave_live || !q_ok) return;
+  float* qrow = dq + qplane + (size_t)my_q * HD;
+#pragma unroll
+  for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * db + 8 * rg + 4 * g;
+      if (d0 < HD)
+        store4<float>(qrow + d0, scale * acc[db][4 * rg], scale * acc[db][4 * rg + 1],
+                      scale * acc[db][4 * rg + 2], scale * acc[db][4 * rg + 3]);
+    }
+}
+
+template <typename T, int HD>
+static void dq_typed(const Dims& d, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dO, float* dq, float* dws, float scale,
+                     hipStream_t stream) {
+  using C = DqCfg<T, HD>;
+  const int nqt = (d.S + C::BM - 1) / C::BM;
+  const int BH = d.B * d.H;
+  dim3 grid((unsigned)(nqt * BH)), block(C::NT);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
+                     (const T*)k, (const T*)v, (const T*)o, lse, (const T*)dO, dq, dws, d.S, d.H,
+                     d.Hkv, nqt, BH, scale * kLog2e, scale);
+}
+
+void launch_bwd_dq(int dtype, const Dims& d, const void* q, const void* k, const void* v,
+                   const void* o, const float* lse, const void* dO, float* dq, float* dws,
+                   float scale, hipStream_t stream) {
+  if (dtype == 0) {
+    if (d.hd == 16) dq_typed<float, 16>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+    else if (d.hd == 32) dq_typed<float, 32>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+    else dq_typed<float, 64>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+  } else {
+    if (d.hd == 16) dq_typed<bf16, 16>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+    else if (d.hd == 32) dq_typed<bf16, 32>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+    else dq_typed<bf16, 64>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+  }
+}
+
+}  // namespace xattn

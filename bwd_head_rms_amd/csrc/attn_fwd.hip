@@ -1,0 +1,197 @@
+// attn_fwd.hip -- fused causal attention forward for gfx950.
+//
+// One workgroup (4 waves) per (batch, head, 128-row query tile); each wave owns
+// 32 query rows.  Key/value tiles of 64 rows are staged through LDS (register
+// prefetch of the next tile overlaps the current tile's arithmetic) and shared
+// by the four waves.  Per tile and wave:
+//   S^T = K . Q^T            (MFMA; keys are rows, queries are lanes, so every
+//                              softmax row lives in one lane pair)
+//   online softmax in the log2 domain: running max m and sum l per query,
+//   P = exp2(S*scale*log2e - m), rescale of the output accumulator by
+//   exp2(m_old - m_new)        (the online softmax of the fused kernel in the
+//                              "xtrain evolution overview", infra table row T14)
+//   O^T += V^T . P^T          (MFMA; P feeds the product from registers)
+// Tiles wholly above the diagonal are never visited; blocks of 32 keys wholly
+// above a wave's rows are skipped; the mask is applied only on tiles that cross
+// the diagonal or the end of the sequence.  The epilogue writes O and the
+// natural-log LSE = (m + log2 l) * ln 2.  Query head h reads kv head
+// h / (H / Hkv) by address (GQA without a copy, row T15 of the same table).
+// Work order: heaviest query tiles first.
+#include "attn_device.hpp"
+#include "launch.hpp"
+
+namespace xattn {
+
+template <typename T, int HD>
+struct FwdCfg {
+  static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
+  static constexpr int RS = HD + Mma<T>::PADR;  // row-major LDS row stride
+  static constexpr int TS = BN + 4;             // transposed LDS row stride
+  static constexpr int ND = HD >= 32 ? HD / 32 : 1;
+  static constexpr int NKS = HD / Mma<T>::KSTEP;  // head-dim contraction steps
+  static constexpr int NAS = 32 / Mma<T>::KSTEP;  // key contraction steps per 32-key block
+  static constexpr bool VT = sizeof(T) == 2;      // bf16 keeps V transposed in LDS
+  static constexpr int K_ELEMS = BN * RS;
+  static constexpr int V_ELEMS = VT ? HD * TS : BN * RS;
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    T* __restrict__ o, float* __restrict__ lse, int S, int H, int Hkv, int nqt, int BH, float c) {
+  using C = FwdCfg<T, HD>;
+  using M = Mma<T>;
+  __shared__ __align__(16) T sK[C::K_ELEMS];
+  __shared__ __align__(16) T sV[C::V_ELEMS];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int li = lane & 31, g = lane >> 5;
+  const int bid = blockIdx.x;
+  const int qt = nqt - 1 - bid / BH;
+  const int bh = bid % BH;
+  const int b = bh / H, h = bh % H;
+  const int kvh = h / (H / Hkv);
+  const T* qp = q + (size_t)bh * S * HD;
+  const T* kp = k + ((size_t)b * Hkv + kvh) * S * HD;
+  const T* vp = v + ((size_t)b * Hkv + kvh) * S * HD;
+
+  const int q0 = qt * C::BM + wave * 32;
+  const int my_q = q0 + li;
+  const bool q_ok = my_q < S;
+  const bool wave_live = q0 < S;
+  const int wave_kv_end = min(S, q0 + 32);  // keys visible to some row of this wave
+
+  typename M::frag qf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks)
+    qf[ks] = q_ok ? row_frag_global<T, HD>(qp + (size_t)my_q * HD, g, ks) : zero_frag<T>();
+
+  f32x16 oacc[C::ND];
+#pragma unroll
+  for (int d = 0; d < C::ND; ++d) oacc[d] = zero_acc();
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_end = min(S, qt * C::BM + C::BM);
+  const int ntiles = (kv_end + C::BN - 1) / C::BN;
+
+  TileStage<T, HD, C::BN, C::NT, true, false> stK;
+  TileStage<T, HD, C::BN, C::NT, !C::VT, C::VT> stV;
+  stK.load(kp, 0, S, tid);
+  stV.load(vp, 0, S, tid);
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kv_t0 = j * C::BN;
+    __syncthreads();
+    stK.template store<C::RS, C::TS>(sK, nullptr, tid);
+    stV.template store<C::RS, C::TS>(sV, sV, tid);
+    __syncthreads();
+    if (j + 1 < ntiles) {
+      stK.load(kp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
+      stV.load(vp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
+    }
+    if (!wave_live || kv_t0 >= wave_kv_end) continue;
+
+    f32x16 s[C::NB];
+    bool act[C::NB];
+#pragma unroll
+    for (int cb = 0; cb < C::NB; ++cb) {
+      act[cb] = kv_t0 + 32 * cb < wave_kv_end;
+      s[cb] = zero_acc();
+      if (act[cb]) {
+        const T* krow = sK + (32 * cb + li) * C::RS;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) M::mma(s[cb], row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
+      }
+    }
+    const bool need_mask = (kv_t0 + C::BN - 1 > q0) || (kv_t0 + C::BN > S);
+    if (need_mask) {
+#pragma unroll
+      for (int cb = 0; cb < C::NB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kv = kv_t0 + 32 * cb + acc_row(r, g);
+          if (!act[cb] || kv > my_q || kv >= S) s[cb][r] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int cb = 0; cb < C::NB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx * c);
+    const float alpha = fast_exp2(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < C::NB; ++cb) {
+      if (!act[cb]) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[cb][r], c, -m_new));
+        s[cb][r] = p;
+        l += p;
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::NAS; ++ks) {
+        const typename M::frag pf = acc_frag<T>(s[cb], ks * M::KPL);
+#pragma unroll
+        for (int db = 0; db < C::ND; ++db) {
+          const int d = min(32 * db + li, HD - 1);
+          typename M::frag a;
+          if constexpr (C::VT)
+            a = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sV) + d * C::TS + 32 * cb, g, ks);
+          else
+            a = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sV) + 32 * cb * C::RS, d, g, ks);
+          M::mma(oacc[db], a, pf);
+        }
+      }
+    }
+  }
+
+  if (!wave_live) return;
+  l += __shfl_xor(l, 32);
+  const float inv = 1.f / l;
+  if (q_ok) {
+    T* orow = o + ((size_t)bh * S + my_q) * HD;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = 32 * db + 8 * rg + 4 * g;
+        if (d0 < HD)
+          store4<T>(orow + d0, oacc[db][4 * rg] * inv, oacc[db][4 * rg + 1] * inv,
+                    oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv);
+      }
+    if (g == 0) lse[(size_t)bh * S + my_q] = (m + fast_log2(l)) * kLn2;
+  }
+}
+
+template <typename T, int HD>
+static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v, void* o,
+                      float* lse, float scale, hipStream_t stream) {
+  using C = FwdCfg<T, HD>;
+  const int nqt = (d.S + C::BM - 1) / C::BM;
+  const int BH = d.B * d.H;
+  dim3 grid((unsigned)(nqt * BH)), block(C::NT);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, block, 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, d.S, d.H, d.Hkv, nqt, BH,
+                     scale * kLog2e);
+}
+
+void launch_fwd(int dtype, const Dims& d, const void* q, const void* k, const void* v, void* o,
+                float* lse, float scale, hipStream_t stream) {
+  if (dtype == 0) {
+    if (d.hd == 16) fwd_typed<float, 16>(d, q, k, v, o, lse, scale, stream);
+    else if (d.hd == 32) fwd_typed<float, 32>(d, q, k, v, o, lse, scale, stream);
+    else fwd_typed<float, 64>(d, q, k, v, o, lse, scale, stream);
+  } else {
+    if (d.hd == 16) fwd_typed<bf16, 16>(d, q, k, v, o, lse, scale, stream);
+    else if (d.hd == 32) fwd_typed<bf16, 32>(d, q, k, v, o, lse, scale, stream);
+    else fwd_typed<bf16, 64>(d, q, k, v, o, lse, scale, stream);
+  }
+}
+
+}  // namespace xattn

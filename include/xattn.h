@@ -1,0 +1,146 @@
+/*
+ * xattn.h -- C ABI of libxattn.so: fused causal scaled-dot-product attention,
+ * forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (after the fused attention kernel of the "xtrain evolution
+ * overview" page, section 一 infra-phase table, row T14, and the batched
+ * attention of the KI-1 fix on "xtrain -- Known Issues & Perf Backlog"):
+ *
+ *   For batch b, query head h, kv head g = h / (H / Hkv) (grouped-query
+ *   attention as in row T15 of the same table: query head h reads kv head
+ *   floor(h / group), no copy of K/V is made), and rows i, j < S:
+ *
+ *     s_ij  = scale * q_i . k_j                      (key j visible iff j <= i)
+ *     P_ij  = exp(s_ij - LSE_i),  LSE_i = ln sum_{j<=i} exp(s_ij)
+ *     o_i   = sum_{j<=i} P_ij v_j
+ *
+ *   and, for an upstream gradient dO, with D_i = sum_d dO_id o_id
+ *   (the row-T14 simplification of the softmax Jacobian):
+ *
+ *     dS_ij = P_ij (dO_i . v_j - D_i)
+ *     dq_i  = scale * sum_{j<=i} dS_ij k_j
+ *     dk_j  = scale * sum_{h in group(g)} sum_{i>=j} dS_ij q_i
+ *     dv_j  =         sum_{h in group(g)} sum_{i>=j} P_ij dO_i
+ *
+ *   The causal mask is top-left aligned (Sq == Sk == S).  No S x S buffer is
+ *   ever allocated.
+ *
+ * Layout: every tensor is contiguous, head-major ("BHSD"):
+ *   q, o, dO, dq : [B][H][S][hd]        k, v, dk, dv : [B][Hkv][S][hd]
+ *   lse          : [B][H][S]            workspace    : see xattn_bwd_workspace_bytes
+ *
+ * Types: q, k, v, o, dO are XATTN_F32 (float) or XATTN_BF16 (bfloat16 bit
+ *   patterns, 2 bytes).  lse, dq, dk, dv and the workspace are always float.
+ *   In bf16 mode products are accumulated in fp32; softmax is fp32; the
+ *   probabilities and dS are rounded to bf16 (nearest-even) before they enter
+ *   a matrix product; o is rounded to bf16 (nearest-even).
+ *
+ * Ownership and execution: all pointers are DEVICE pointers owned by the
+ *   caller.  The library never allocates, frees or synchronises, keeps no
+ *   global state, and only enqueues kernels on `stream` (a hipStream_t; NULL
+ *   means the legacy default stream) before returning.  Outputs are fully
+ *   overwritten, never accumulated.  Inputs are never modified.  Outputs must
+ *   not alias inputs or each other.  Device faults surface at the caller's next
+ *   synchronisation, as with any asynchronous HIP call.
+ *
+ * Errors: every argument is validated on the host before any HIP call; an
+ *   invalid call returns its status code and enqueues nothing.  A failed
+ *   kernel launch returns XATTN_ERR_HIP.
+ *
+ * Supported: hd in {16, 32, 64}; any S >= 1; H a multiple of Hkv; scale a
+ *   positive finite number; every data pointer 16-byte aligned; every tensor
+ *   below 2^31 elements per (batch, head) plane and B*H*ceil(S/128) below
+ *   2^31 workgroups.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  XATTN_F32 = 0,
+  XATTN_BF16 = 1
+} xattn_dtype;
+
+typedef enum {
+  XATTN_OK = 0,
+  XATTN_ERR_NULL = 1,       /* a required pointer is NULL */
+  XATTN_ERR_SHAPE = 2,      /* B, S, H, Hkv or hd <= 0, or a size limit exceeded */
+  XATTN_ERR_GQA = 3,        /* H is not a multiple of Hkv */
+  XATTN_ERR_HEAD_DIM = 4,   /* hd not in {16, 32, 64} */
+  XATTN_ERR_DTYPE = 5,      /* dtype is not an xattn_dtype */
+  XATTN_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required */
+  XATTN_ERR_SCALE = 7,      /* scale not positive and finite */
+  XATTN_ERR_HIP = 8,        /* the HIP runtime rejected a kernel launch */
+  XATTN_ERR_ALIGN = 9       /* a data pointer is not 16-byte aligned */
+} xattn_status;
+
+/*
+ * Forward (row T14 of the infra table: online softmax tiled over KV, the
+ * per-row logsumexp kept for the backward).
+ *   q [B][H][S][hd], k and v [B][Hkv][S][hd] in `dtype`  (inputs)
+ *   o [B][H][S][hd] in `dtype`, lse [B][H][S] float      (outputs)
+ *   lse is the natural-log logsumexp of the scaled, masked scores.
+ * Returns an xattn_status.
+ */
+int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int S, int H, int Hkv, int hd, float scale, int dtype,
+              void* stream);
+
+/*
+ * Bytes of device workspace xattn_bwd needs: 4*B*H*S (the per-row D values),
+ * O(B*H*S), never S x S.  Returns 0 for invalid shapes.
+ */
+size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype);
+
+/*
+ * Backward (row T14: scores recomputed from q, k and lse; D = rowsum(dO * o);
+ * row T15: dk/dv summed over the query heads of each kv group in a fixed
+ * order, no atomics, so results are bitwise reproducible run to run).
+ *   q, o, dO [B][H][S][hd] and k, v [B][Hkv][S][hd] in `dtype`, lse [B][H][S]
+ *   float (inputs; o and lse may come from any source, e.g. xattn_fwd)
+ *   dq [B][H][S][hd], dk and dv [B][Hkv][S][hd] float (outputs)
+ *   workspace: device scratch of at least xattn_bwd_workspace_bytes(...) bytes,
+ *   16-byte aligned; its contents on entry do not matter.
+ * Two kernels are enqueued in order on `stream`.
+ * Returns an xattn_status.
+ */
+int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dO, float* dq, float* dk, float* dv,
+              int B, int S, int H, int Hkv, int hd, float scale, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two halves of xattn_bwd, for callers that schedule them separately
+ * (e.g. to overlap the query-side half with other work, or to time each).
+ * xattn_bwd(...) is exactly xattn_bwd_dq(...) followed on the same stream by
+ * xattn_bwd_dkdv(...) with the same arguments and workspace.
+ *
+ * xattn_bwd_dq: writes dq [B][H][S][hd] float and stores D = rowsum(dO * o)
+ *   ([B][H][S] float) in the workspace.
+ * xattn_bwd_dkdv: writes dk, dv [B][Hkv][S][hd] float; reads D from the
+ *   workspace, so it must be ordered after an xattn_bwd_dq call with the same
+ *   q, o, dO, lse, shapes and workspace.
+ * Argument meaning, layout, validation and status codes are those of xattn_bwd.
+ */
+int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dO, float* dq, int B, int S, int H, int Hkv, int hd, float scale,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                   const void* dO, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
+                   float scale, int dtype, const void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* xattn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

@@ -1,0 +1,147 @@
+"""C ABI of libxattn.so on the CPU: the library loads, exports every symbol the
+headers declare, and rejects every invalid argument with its status code before
+any HIP call (no compute call is made here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from bwd_head_rms_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, GQA, HEAD_DIM, DTYPE, WORKSPACE, SCALE, HIP, ALIGN = range(10)
+
+P = 0x10000  # a non-NULL, 16-byte aligned stand-in pointer; never dereferenced
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        names |= set(re.findall(r"^[A-Za-z_][\w \t\*]*?\b(xattn_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert names == set(_lib.SYMBOLS), names
+    for n in names:
+        assert hasattr(L, n), f"libxattn.so does not export {n}"
+
+
+def test_nm_shows_c_linkage():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    for n in declared_symbols():
+        assert re.search(rf"\bT {n}$", out, flags=re.M), f"{n} is not an exported C symbol"
+
+
+def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, S=16, H=2, Hkv=2, hd=16, scale=0.25, dtype=0):
+    return L.xattn_fwd(q, k, v, o, lse, B, S, H, Hkv, hd, scale, dtype, None)
+
+
+def bwd(L, ws=P, ws_bytes=None, B=1, S=16, H=2, Hkv=2, hd=16, scale=0.25, dtype=0, **ptrs):
+    p = {n: P for n in ("q", "k", "v", "o", "lse", "dO", "dq", "dk", "dv")}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = 4 * B * H * S
+    return L.xattn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"], p["dk"], p["dv"],
+                       B, S, H, Hkv, hd, scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_fwd_null_pointer(L, name):
+    assert fwd(L, **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse", "dO", "dq", "dk", "dv"])
+def test_bwd_null_pointer(L, name):
+    assert bwd(L, **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("S", 0), ("H", 0), ("Hkv", 0), ("hd", 0),
+                                         ("B", -1), ("S", -5)])
+def test_nonpositive_dims(L, field, value):
+    assert fwd(L, **{field: value}) == SHAPE
+    assert bwd(L, **{field: value}) == SHAPE
+
+
+def test_gqa_divisibility(L):
+    assert fwd(L, H=6, Hkv=4) == GQA
+    assert bwd(L, H=6, Hkv=4) == GQA
+
+
+@pytest.mark.parametrize("hd", [8, 24, 48, 128, 256])
+def test_unsupported_head_dim(L, hd):
+    assert fwd(L, hd=hd) == HEAD_DIM
+    assert bwd(L, hd=hd) == HEAD_DIM
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 7])
+def test_unknown_dtype(L, dtype):
+    assert fwd(L, dtype=dtype) == DTYPE
+    assert bwd(L, dtype=dtype) == DTYPE
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.5, float("inf"), float("nan")])
+def test_bad_scale(L, scale):
+    assert fwd(L, scale=scale) == SCALE
+    assert bwd(L, scale=scale) == SCALE
+
+
+def test_workspace_size_and_checks(L):
+    assert L.xattn_bwd_workspace_bytes(4, 2048, 16, 16, 64, 1) == 4 * 4 * 16 * 2048
+    assert L.xattn_bwd_workspace_bytes(16, 1024, 8, 2, 64, 0) == 4 * 16 * 8 * 1024
+    assert L.xattn_bwd_workspace_bytes(1, 16, 3, 2, 16, 0) == 0  # invalid GQA shape
+    assert L.xattn_bwd_workspace_bytes(1, 16, 2, 2, 16, 9) == 0  # invalid dtype
+    assert bwd(L, ws=None) == WORKSPACE
+    assert bwd(L, ws_bytes=4 * 2 * 16 - 1) == WORKSPACE
+
+
+def test_size_limits(L):
+    # one (batch, head) plane must stay below 2^31 elements
+    assert fwd(L, S=2 ** 26, hd=64) == SHAPE
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_fwd_misaligned(L, name):
+    assert fwd(L, **{name: P + 4}) == ALIGN
+
+
+@pytest.mark.parametrize("name", ["q", "dO", "dq", "dk", "dv", "ws"])
+def test_bwd_misaligned(L, name):
+    assert bwd(L, **{name: P + 8}) == ALIGN
+
+
+def test_strerror_covers_every_status(L):
+    seen = set()
+    for s in range(10):
+        msg = L.xattn_strerror(s)
+        assert isinstance(msg, bytes) and msg
+        seen.add(msg)
+    assert len(seen) == 10
+    assert L.xattn_strerror(12345) == b"unknown xattn status"
+
+
+def test_product_path_has_no_fallback(monkeypatch, tmp_path):
+    """Without the built library the binding raises; it never computes elsewhere."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(_lib.XattnError):
+        _lib.lib()
+
+
+def test_product_package_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "bwd_head_rms_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+            text = open(path).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), path
+            assert "xattn_ref" not in text and "ref_attn" not in text, path

@@ -1,0 +1,141 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+* every named workload at its full size, in the launch configuration the
+  benchmark times; the oracle runs on all (batch, kv head) units where it
+  finishes in seconds, else on sampled units (first, middle, last);
+* the backward fed the oracle's own o (rounded to the input dtype) and lse;
+* ragged and edge shapes spanning several tiles and a partial tail, S = 1,
+  GQA groups, every head dimension, both dtypes;
+* a long sequence checked on an exact prefix (causality makes rows < t of o,
+  lse and dq depend only on the first t positions) and by identities.
+"""
+import numpy as np
+import pytest
+
+import gpu_helpers as H
+from bwd_head_rms_amd import inputs
+from oracle import default
+
+pytestmark = pytest.mark.gpu
+
+# Units the oracle computes for each workload (None = all of them).
+SAMPLED = {
+    "tiny_b1_s16_h2_hd16_f32": None,
+    "dim384_b16_s256_h12_hd32_f32": None,
+    "dim384_b32_s256_h12_hd32_bf16": None,
+    "gqa_b16_s1024_h8_kv2_hd64_f32": [0, 15, 31],
+    "gqa_b16_s1024_h8_kv2_hd64_bf16": [0, 15, 31],
+    "long_b4_s2048_h16_hd64_bf16": [0, 21, 42, 63],
+}
+
+
+@pytest.fixture(scope="module")
+def ref():
+    return default()
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_parity(name, ref):
+    w = inputs.WORKLOADS[name]
+    H.log(f"parity {w.describe()}")
+    arrs = inputs.generate_workload(w)
+    gpu = H.gpu_run(arrs, w.dtype, w.scale)
+    units = SAMPLED[name]
+    if units is None:
+        r = ref.run(arrs["q"], arrs["k"], arrs["v"], arrs["dO"], scale=w.scale)
+        H.compare(gpu, r, w.dtype, name)
+    else:
+        outs = [ref.run(arrs["q"], arrs["k"], arrs["v"], arrs["dO"], scale=w.scale, units=(u, u + 1))
+                for u in units]
+        merged = {n: np.where(np.isnan(outs[0][n]), 0.0, outs[0][n]) for n in H.NAMES}
+        for o in outs[1:]:
+            for n in H.NAMES:
+                merged[n] = np.where(np.isnan(o[n]), merged[n], o[n])
+        H.compare(gpu, merged, w.dtype, name, units=units, Hkv=w.Hkv, group=w.group)
+
+
+@pytest.mark.parametrize("name", ["tiny_b1_s16_h2_hd16_f32", "dim384_b16_s256_h12_hd32_f32",
+                                  "dim384_b32_s256_h12_hd32_bf16"])
+def test_isolated_backward_from_oracle_forward(name, ref):
+    """bwd fed the oracle's o (rounded to the dtype) and lse: the backward is
+    checked on its own, independent of the GPU forward."""
+    import torch
+    from bwd_head_rms_amd import api
+    w = inputs.WORKLOADS[name]
+    H.log(f"isolated bwd {w.describe()}")
+    arrs = inputs.generate_workload(w)
+    r = ref.run(arrs["q"], arrs["k"], arrs["v"], arrs["dO"], scale=w.scale)
+    t = H.to_dev(arrs, w.dtype)
+    o = inputs.to_torch(r["o"].astype(np.float32), w.dtype, "cuda")
+    lse = torch.from_numpy(r["lse"].astype(np.float32)).cuda()
+    dq, dk, dv = api.bwd(t["q"], t["k"], t["v"], o, lse, t["dO"], w.scale)
+    torch.cuda.synchronize()
+    gpu = {"dq": dq.cpu().double().numpy(), "dk": dk.cpu().double().numpy(),
+           "dv": dv.cpu().double().numpy()}
+    H.compare(gpu, r, w.dtype, f"isolated bwd {name}", names=("dq", "dk", "dv"))
+
+
+EDGE = [
+    # B, S, H, Hkv, hd, dtype
+    (1, 1, 1, 1, 16, "f32"),
+    (1, 1, 2, 1, 64, "bf16"),
+    (2, 2, 2, 2, 32, "f32"),
+    (2, 17, 3, 1, 32, "f32"),
+    (1, 33, 4, 2, 64, "bf16"),
+    (2, 100, 2, 2, 16, "bf16"),
+    (1, 127, 8, 2, 64, "f32"),
+    (1, 129, 6, 2, 64, "f32"),
+    (1, 200, 4, 4, 32, "bf16"),
+    (1, 257, 2, 1, 64, "bf16"),
+    (3, 64, 2, 2, 32, "f32"),
+    (1, 384, 2, 2, 64, "bf16"),
+    (1, 300, 4, 1, 16, "f32"),
+    (2, 191, 6, 3, 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "B{}_S{}_H{}_Hkv{}_hd{}_{}".format(*s))
+def test_edge_shapes(shape, ref):
+    B, S, Hq, Hkv, hd, dtype = shape
+    H.log(f"edge {shape}")
+    arrs = inputs.generate(B, S, Hq, Hkv, hd, seed=1000 + S, shaped=True, dtype=dtype)
+    scale = 1.0 / np.sqrt(hd)
+    gpu = H.gpu_run(arrs, dtype, scale)
+    r = ref.run(arrs["q"], arrs["k"], arrs["v"], arrs["dO"], scale=scale)
+    H.compare(gpu, r, dtype, f"edge {shape}", terms=H.term_sizes(arrs, scale))
+
+
+def test_unshaped_inputs_and_other_scale(ref):
+    """Raw N(0,1) q/k (no QK-norm) with a larger scale: sharper softmax rows."""
+    B, S, Hq, Hkv, hd = 2, 150, 4, 2, 64
+    for dtype in ("f32", "bf16"):
+        arrs = inputs.generate(B, S, Hq, Hkv, hd, seed=77, shaped=False, dtype=dtype)
+        gpu = H.gpu_run(arrs, dtype, 0.5)
+        r = ref.run(arrs["q"], arrs["k"], arrs["v"], arrs["dO"], scale=0.5)
+        H.compare(gpu, r, dtype, f"unshaped scale 0.5 {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_long_sequence_prefix_and_identities(dtype, ref):
+    """S = 8192: rows < t of o, lse, dq against the oracle on the first t
+    positions; dk/dv by the exact identities sum_j dv_j = sum_i dO_i and
+    sum_i q_i.dq_i = sum_j k_j.dk_j (per batch, kv head)."""
+    B, S, Hq, Hkv, hd, t = 1, 8192, 2, 1, 64, 384
+    H.log(f"long S={S} {dtype}")
+    arrs = inputs.generate(B, S, Hq, Hkv, hd, seed=88, shaped=True, dtype=dtype)
+    scale = 1.0 / np.sqrt(hd)
+    gpu = H.gpu_run(arrs, dtype, scale)
+    pre = {n: a[:, :, :t] for n, a in arrs.items()}
+    r = ref.run(pre["q"], pre["k"], pre["v"], pre["dO"], scale=scale)
+    gp = {n: gpu[n][:, :, :t] for n in ("o", "lse", "dq")}
+    H.compare(gp, r, dtype, f"long S={S} prefix {t}", names=("o", "lse", "dq"))
+    q, k, dO = (arrs[n].astype(np.float64) for n in ("q", "k", "dO"))
+    tau = H.TAU[dtype]
+    lhs = gpu["dv"][0, 0].sum(axis=0)
+    rhs = dO[0].sum(axis=(0, 1))
+    assert np.max(np.abs(lhs - rhs)) <= tau * np.max(np.abs(rhs)) + 1e-3, "sum_j dv_j != sum_i dO_i"
+    qd = float(np.sum(q[0] * gpu["dq"][0]))
+    kd = float(np.sum(k[0, 0] * gpu["dk"][0, 0]))
+    mag = float(np.sum(np.abs(q[0] * gpu["dq"][0])))
+    assert abs(qd - kd) <= tau * mag, f"q.dq {qd} != k.dk {kd} (magnitude {mag})"
