@@ -49,12 +49,16 @@ MEASURED_TRAFFIC = {
 
 
 def kernel_source_hash(kernel):
+    """sha256 prefix of a kernel's sources and the device compile flags."""
     import hashlib
+
+    from bwd_head_rms_amd import build
     csrc = os.path.join(ROOT, "bwd_head_rms_amd", "csrc")
     h = hashlib.sha256()
     for f in (KERNEL_FILES[kernel], "attn_device.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(build.COMMON + build.DEVICE_FLAGS).encode())
     return h.hexdigest()[:16]
 
 

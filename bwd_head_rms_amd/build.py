@@ -18,8 +18,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["attn_fwd.hip", "attn_bwd_dq.hip", "attn_bwd_dkdv.hip", "api.cpp"]
 
-# Packed-fp32 VALU instructions are switched off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 VALU instructions are switched off for all device code.  MFMA
+# accumulators are kept in ordinary VGPRs: the kernels post-process every score
+# tile with VALU code, and the AGPR form made the compiler copy each tile
+# between the two register files.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 
