@@ -16,6 +16,8 @@
 // "xtrain evolution overview", infra table row T15).  D comes from the dq
 // kernel, which runs first on the same stream.  Work order: heaviest key tiles
 // (those near the start of the sequence) first.
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "launch.hpp"
 
@@ -111,11 +113,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     if (it + 1 < iters) prefetch(it + 1);
     if (!wave_live) continue;
 
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
+    // One 32-row query block.  Blocks are 32-aligned like the wave's keys, so a
+    // block is either wholly visible, the diagonal block, or wholly masked
+    // (skipped); only the diagonal block and the sequence tail carry a mask.
+    auto block = [&](const int qb, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int qb0 = qt * C::BMQ + 32 * qb;
-      if (qb0 + 31 < kv0 || qb0 >= S) continue;  // wholly above the diagonal, or past S
-      const bool need_mask = (kv0 + 31 > qb0) || (qb0 + 32 > S);
       f32x16 s = zero_acc(), dp = zero_acc();
       const T* qrow = sQ + (32 * qb + li) * C::RS;
       const T* orow = sO + (32 * qb + li) * C::RS;
@@ -128,9 +131,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) {
         const int ql = 32 * qb + acc_row(r, g);
         float p = fast_exp2(fmaf(s[r], c, -sL[ql]));
-        if (need_mask) {
-          const int qi = qt * C::BMQ + ql;
-          if (my_kv > qi || qi >= S) p = 0.f;
+        if constexpr (MASK) {
+          const int qi = qb0 + acc_row(r, g);
+          p = (qi >= my_kv && qi < S) ? p : 0.f;
         }
         s[r] = p;
         dp[r] = p * (dp[r] - sD[ql]);  // dS
@@ -154,6 +157,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           M::mma(dkacc[db], aq, sf);
         }
       }
+    };
+
+#pragma unroll
+    for (int qb = 0; qb < C::NQB; ++qb) {
+      const int qb0 = qt * C::BMQ + 32 * qb;
+      if (qb0 + 31 < kv0 || qb0 >= S) continue;  // wholly above the diagonal, or past S
+      if (qb0 < kv0 + 32 || qb0 + 32 > S)
+        block(qb, std::true_type{});
+      else
+        block(qb, std::false_type{});
     }
   }
 

@@ -13,6 +13,8 @@
 // and dq = scale * dQ is written in fp32.  K, K^T (bf16 only) and V tiles are
 // staged through LDS with register prefetch; query head h reads kv head
 // h / (H / Hkv) by address.
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "launch.hpp"
 
@@ -107,11 +109,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       stV.load(vp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
     }
     if (!wave_live || kv_t0 >= wave_kv_end) continue;
-    const bool need_mask = (kv_t0 + C::BN - 1 > q0) || (kv_t0 + C::BN > S);
-
-#pragma unroll
-    for (int cb = 0; cb < C::NB; ++cb) {
-      if (kv_t0 + 32 * cb >= wave_kv_end) continue;
+    // One 32-key block.  Key blocks are 32-aligned like the wave's rows, so a
+    // visited block is either wholly visible or the diagonal block; only the
+    // diagonal block and the sequence tail carry a mask.
+    auto block = [&](const int cb, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int kb0 = kv_t0 + 32 * cb;
       f32x16 s = zero_acc(), dp = zero_acc();
       const T* krow = sK + (32 * cb + li) * C::RS;
       const T* vrow = sV + (32 * cb + li) * C::RS;
@@ -123,9 +126,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[r], c, -lse2));
-        if (need_mask) {
-          const int kv = kv_t0 + 32 * cb + acc_row(r, g);
-          if (kv > my_q || kv >= S) p = 0.f;
+        if constexpr (MASK) {
+          const int kv = kb0 + acc_row(r, g);
+          p = (kv <= my_q && kv < S) ? p : 0.f;
         }
         s[r] = p * (dp[r] - Drow);  // dS^T
       }
@@ -143,6 +146,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
           M::mma(acc[db], a, sf);
         }
       }
+    };
+
+#pragma unroll
+    for (int cb = 0; cb < C::NB; ++cb) {
+      const int kb0 = kv_t0 + 32 * cb;
+      if (kb0 >= wave_kv_end) continue;  // wholly above this wave's rows, or past S
+      if (kb0 + 31 > q0 || kb0 + 32 > S)
+        block(cb, std::true_type{});
+      else
+        block(cb, std::false_type{});
     }
   }
 

@@ -6,14 +6,15 @@
 // by the four waves.  Per tile and wave:
 //   S^T = K . Q^T            (MFMA; keys are rows, queries are lanes, so every
 //                              softmax row lives in one lane pair)
-//   online softmax in the log2 domain: running max m and sum l per query,
+//   online softmax in the log2 domain: reference max m and sum l per query,
 //   P = exp2(S*scale*log2e - m), rescale of the output accumulator by
-//   exp2(m_old - m_new)        (the online softmax of the fused kernel in the
-//                              "xtrain evolution overview", infra table row T14)
+//   exp2(m_old - m_new) when a row's max grows past its slack (the online
+//   softmax of the fused kernel in the "xtrain evolution overview", infra
+//   table row T14)
 //   O^T += V^T . P^T          (MFMA; P feeds the product from registers)
 // Tiles wholly above the diagonal are never visited; blocks of 32 keys wholly
-// above a wave's rows are skipped; the mask is applied only on tiles that cross
-// the diagonal or the end of the sequence.  The epilogue writes O and the
+// above a wave's rows are skipped; the mask is applied only on the diagonal
+// block and at the end of the sequence.  The epilogue writes O and the
 // natural-log LSE = (m + log2 l) * ln 2.  Query head h reads kv head
 // h / (H / Hkv) by address (GQA without a copy, row T15 of the same table).
 // Work order: heaviest query tiles first.
@@ -21,6 +22,11 @@
 #include "launch.hpp"
 
 namespace xattn {
+
+// Slack (log2 units) a row's scores may exceed its reference max before the
+// output accumulator is rescaled: probabilities stay below 2^8 = 256, far
+// from fp32 or bf16 overflow, and the sum l below 256 * S.
+constexpr float kRescaleSlack = 8.f;
 
 template <typename T, int HD>
 struct FwdCfg {
@@ -91,46 +97,58 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     }
     if (!wave_live || kv_t0 >= wave_kv_end) continue;
 
+    // Scores of the (up to) two 32-key blocks of this tile.  Key blocks are
+    // 32-aligned like the wave's rows: a visited block is wholly visible or the
+    // diagonal block, and only the diagonal block and the sequence tail carry a
+    // mask (masked scores become -inf, i.e. weight exactly 0).
     f32x16 s[C::NB];
     bool act[C::NB];
 #pragma unroll
     for (int cb = 0; cb < C::NB; ++cb) {
-      act[cb] = kv_t0 + 32 * cb < wave_kv_end;
+      const int kb0 = kv_t0 + 32 * cb;
+      act[cb] = kb0 < wave_kv_end;
       s[cb] = zero_acc();
       if (act[cb]) {
         const T* krow = sK + (32 * cb + li) * C::RS;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) M::mma(s[cb], row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
-      }
-    }
-    const bool need_mask = (kv_t0 + C::BN - 1 > q0) || (kv_t0 + C::BN > S);
-    if (need_mask) {
+        if (kb0 + 31 > q0 || kb0 + 32 > S) {
 #pragma unroll
-      for (int cb = 0; cb < C::NB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kv = kv_t0 + 32 * cb + acc_row(r, g);
-          if (!act[cb] || kv > my_q || kv >= S) s[cb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int kv = kb0 + acc_row(r, g);
+            s[cb][r] = (kv <= my_q && kv < S) ? s[cb][r] : -INFINITY;
+          }
         }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int cb = 0; cb < C::NB; ++cb)
+      if (act[cb]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * c);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
-    l *= alpha;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    // Lazy rescale: a row keeps its reference max m while its scores stay
+    // below m + kRescaleSlack (log2 units), so P <= 2^kRescaleSlack and the
+    // accumulator is rescaled only when some row's max really grows.  The
+    // decision is per row (rows that do not need it multiply by exactly 1),
+    // so every row's result depends only on that row's scores.
+    const bool grow = mx > m + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m;
+      const float alpha = grow ? fast_exp2(m - m_new) : 1.f;
+      m = m_new;
+      l *= alpha;
 #pragma unroll
-    for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
+    }
 #pragma unroll
     for (int cb = 0; cb < C::NB; ++cb) {
       if (!act[cb]) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[cb][r], c, -m_new));
+        const float p = fast_exp2(fmaf(s[cb][r], c, -m));
         s[cb][r] = p;
         l += p;
       }

@@ -83,9 +83,10 @@ def test_constant_values_give_constant_output(dtype):
     arrs = _gen(1, 400, 2, 2, 64, dtype)
     arrs["v"] = np.ones_like(arrs["v"])
     out = H.gpu_run(arrs, dtype)
-    tol = 1e-6 if dtype == "f32" else 1e-2
-    assert np.max(np.abs(out["o"] - 1.0)) <= tol
-    assert np.max(np.abs(out["dq"])) <= (1e-5 if dtype == "f32" else 2e-2) * max(1.0, np.max(np.abs(arrs["dO"])))
+    tau = H.TAU[dtype]  # the parity tolerance, relative to max|o| = 1
+    assert np.max(np.abs(out["o"] - 1.0)) <= tau
+    # dq = 0 exactly in real arithmetic; bound it by tau times one summand's size
+    assert np.max(np.abs(out["dq"])) <= tau * H.term_sizes(arrs, 1.0 / np.sqrt(64))["dq"]
 
 
 def test_key_shift_invariance_f32():
