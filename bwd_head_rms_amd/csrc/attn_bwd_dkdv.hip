@@ -3,13 +3,15 @@
 // One workgroup (4 waves) per (batch, kv head, 128-row key tile); each wave owns
 // 32 key rows whose K and V operands stay in registers for the whole kernel.
 // The workgroup walks every query head of its GQA group (r ascending) and, for
-// each, the 64-row query tiles at or below the diagonal (ascending), staging Q,
-// dO (row-major, plus transposed copies for bf16), LSE and D through LDS with
-// register prefetch.  Per 32-row query block and wave:
+// each, the query tiles (128 rows for bf16, 64 for fp32) at or below the
+// diagonal (ascending), staging Q, dO, LSE and D row-major through a
+// double-buffered LDS ring (one barrier per tile).  Per 32-row query block and
+// wave:
 //   S  = Q . K^T,   P = exp2(S*scale*log2e - LSE_i*log2e)     (recompute)
 //   dP = dO . V^T,  dS = P * (dP - D_i)
-//   dV^T += dO^T . P          (P feeds the product from registers)
-//   dK^T += Q^T . dS
+//   dV^T += dO^T . P          (P feeds the product from registers; dO^T and
+//   dK^T += Q^T . dS           Q^T come from the row-major tiles by transpose
+//                              reads)
 // dk = scale * dK and dv are written in fp32 once.  The GQA group sum happens in
 // registers in a fixed order (head r, then query tile), with no atomics, so the
 // result is bitwise reproducible (the deterministic group sum of the
@@ -25,15 +27,14 @@ namespace xattn {
 
 template <typename T, int HD>
 struct DkvCfg {
-  static constexpr int NW = 4, NT = NW * kWave, BN = 32 * NW, BMQ = 64, NQB = BMQ / 32;
+  static constexpr int NW = 4, NT = NW * kWave, BN = 32 * NW;
+  static constexpr int BMQ = sizeof(T) == 2 ? 128 : 64;  // query rows per staged tile
+  static constexpr int NQB = BMQ / 32;
   static constexpr int RS = HD + Mma<T>::PADR;
-  static constexpr int TS = BMQ + 4;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;
   static constexpr int NAS = 32 / Mma<T>::KSTEP;
-  static constexpr bool TR = sizeof(T) == 2;  // bf16 keeps Q and dO transposed too
-  static constexpr int R_ELEMS = BMQ * RS;
-  static constexpr int T_ELEMS = TR ? HD * TS : 8;
+  static constexpr int TILE = BMQ * RS;
 };
 
 template <typename T, int HD>
@@ -44,12 +45,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     float c, float scale) {
   using C = DkvCfg<T, HD>;
   using M = Mma<T>;
-  __shared__ __align__(16) T sQ[C::R_ELEMS];
-  __shared__ __align__(16) T sQt[C::T_ELEMS];
-  __shared__ __align__(16) T sO[C::R_ELEMS];   // dO, row-major
-  __shared__ __align__(16) T sOt[C::T_ELEMS];  // dO, transposed (bf16)
-  __shared__ float sL[C::BMQ];                 // LSE * log2e
-  __shared__ float sD[C::BMQ];
+  __shared__ __align__(16) T sQ[2][C::TILE];
+  __shared__ __align__(16) T sO[2][C::TILE];  // dO
+  __shared__ float sL[2][C::BMQ];             // LSE * log2e
+  __shared__ float sD[2][C::BMQ];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 31, g = lane >> 5;
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int per_head = nq - qt_first;
   const int iters = group * per_head;
 
-  TileStage<T, HD, C::BMQ, C::NT, true, C::TR> stQ, stO;
+  TileStage<T, HD, C::BMQ, C::NT> stQ, stO;
   float pre_l = 0.f, pre_d = 0.f;
   auto prefetch = [&](int it) {
     const int r = it / per_head, qt = qt_first + it % per_head;
@@ -98,76 +97,95 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       pre_d = qi < S ? dws[bh * S + qi] : 0.f;
     }
   };
-  if (iters > 0) prefetch(0);
+  auto stage = [&](int buf) {
+    stQ.template store<C::RS>(sQ[buf], tid);
+    stO.template store<C::RS>(sO[buf], tid);
+    if (tid < C::BMQ) {
+      sL[buf][tid] = pre_l;
+      sD[buf][tid] = pre_d;
+    }
+  };
+  prefetch(0);
+  stage(0);
+  if (iters > 1) prefetch(1);
+  __syncthreads();
 
   for (int it = 0; it < iters; ++it) {
+    const int cur = it & 1;
     const int qt = qt_first + it % per_head;
-    __syncthreads();
-    stQ.template store<C::RS, C::TS>(sQ, sQt, tid);
-    stO.template store<C::RS, C::TS>(sO, sOt, tid);
-    if (tid < C::BMQ) {
-      sL[tid] = pre_l;
-      sD[tid] = pre_d;
+    if (it + 1 < iters) {  // the other buffer was last read before the previous barrier
+      stage(cur ^ 1);
+      if (it + 2 < iters) prefetch(it + 2);
     }
-    __syncthreads();
-    if (it + 1 < iters) prefetch(it + 1);
-    if (!wave_live) continue;
-
-    // One 32-row query block.  Blocks are 32-aligned like the wave's keys, so a
-    // block is either wholly visible, the diagonal block, or wholly masked
-    // (skipped); only the diagonal block and the sequence tail carry a mask.
-    auto block = [&](const int qb, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      const int qb0 = qt * C::BMQ + 32 * qb;
-      f32x16 s = zero_acc(), dp = zero_acc();
-      const T* qrow = sQ + (32 * qb + li) * C::RS;
-      const T* orow = sO + (32 * qb + li) * C::RS;
+    if (wave_live) {
+      const T* tQ = sQ[cur];
+      const T* tO = sO[cur];
+      const float* tL = sL[cur];
+      const float* tD = sD[cur];
+      // One 32-row query block.  Blocks are 32-aligned like the wave's keys, so
+      // a block is either wholly visible, the diagonal block, or wholly masked
+      // (skipped); only the diagonal block and the sequence tail carry a mask.
+      auto block = [&](const int qb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int qb0 = qt * C::BMQ + 32 * qb;
+        f32x16 s = zero_acc(), dp = zero_acc();
+        const T* qrow = tQ + (32 * qb + li) * C::RS;
+        const T* orow = tO + (32 * qb + li) * C::RS;
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        M::mma(s, row_frag_lds<T, HD>(qrow, g, ks), kf[ks]);
-        M::mma(dp, row_frag_lds<T, HD>(orow, g, ks), vf[ks]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 32 * qb + acc_row(r, g);
-        float p = fast_exp2(fmaf(s[r], c, -sL[ql]));
-        if constexpr (MASK) {
-          const int qi = qb0 + acc_row(r, g);
-          p = (qi >= my_kv && qi < S) ? p : 0.f;
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          M::mma(s, row_frag_lds<T, HD>(qrow, g, ks), kf[ks]);
+          M::mma(dp, row_frag_lds<T, HD>(orow, g, ks), vf[ks]);
         }
-        s[r] = p;
-        dp[r] = p * (dp[r] - sD[ql]);  // dS
-      }
 #pragma unroll
-      for (int ks = 0; ks < C::NAS; ++ks) {
-        const typename M::frag pf = acc_frag<T>(s, ks * M::KPL);
-        const typename M::frag sf = acc_frag<T>(dp, ks * M::KPL);
-#pragma unroll
-        for (int db = 0; db < C::ND; ++db) {
-          const int d = min(32 * db + li, HD - 1);
-          typename M::frag ao, aq;
-          if constexpr (C::TR) {
-            ao = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sOt) + d * C::TS + 32 * qb, g, ks);
-            aq = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sQt) + d * C::TS + 32 * qb, g, ks);
-          } else {
-            ao = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sO) + 32 * qb * C::RS, d, g, ks);
-            aq = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sQ) + 32 * qb * C::RS, d, g, ks);
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 32 * qb + acc_row(r, g);
+          float p = fast_exp2(fmaf(s[r], c, -tL[ql]));
+          if constexpr (MASK) {
+            const int qi = qb0 + acc_row(r, g);
+            p = (qi >= my_kv && qi < S) ? p : 0.f;
           }
-          M::mma(dvacc[db], ao, pf);
-          M::mma(dkacc[db], aq, sf);
+          s[r] = p;
+          dp[r] = p * (dp[r] - tD[ql]);  // dS
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::NAS; ++ks) {
+          const typename M::frag pf = acc_frag<T>(s, ks * M::KPL);
+          const typename M::frag sf = acc_frag<T>(dp, ks * M::KPL);
+#pragma unroll
+          for (int db = 0; db < C::ND; ++db) {
+            typename M::frag ao, aq;
+            if constexpr (sizeof(T) == 2) {
+              ao = accrow_frag_bf16<HD, C::RS>(tO, 32 * qb + 16 * ks, 32 * db, lane);
+              aq = accrow_frag_bf16<HD, C::RS>(tQ, 32 * qb + 16 * ks, 32 * db, lane);
+            } else {
+              const int d = min(32 * db + li, HD - 1);
+              ao = accrow_frag_f32<C::RS>(tO + 32 * qb * C::RS, d, g, ks);
+              aq = accrow_frag_f32<C::RS>(tQ + 32 * qb * C::RS, d, g, ks);
+            }
+            M::mma(dvacc[db], ao, pf);
+            M::mma(dkacc[db], aq, sf);
+          }
+        }
+      };
+
+      const int qt0 = qt * C::BMQ;
+      if (qt0 >= kv0 + 32 && qt0 + C::BMQ <= S) {
+        // every block of the tile is below the diagonal and inside the sequence
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) block(qb, std::false_type{});
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < C::NQB; ++qb) {
+          const int qb0 = qt0 + 32 * qb;
+          if (qb0 + 31 < kv0 || qb0 >= S) continue;  // wholly above the diagonal, or past S
+          if (qb0 < kv0 + 32 || qb0 + 32 > S)
+            block(qb, std::true_type{});
+          else
+            block(qb, std::false_type{});
         }
       }
-    };
-
-#pragma unroll
-    for (int qb = 0; qb < C::NQB; ++qb) {
-      const int qb0 = qt * C::BMQ + 32 * qb;
-      if (qb0 + 31 < kv0 || qb0 >= S) continue;  // wholly above the diagonal, or past S
-      if (qb0 < kv0 + 32 || qb0 + 32 > S)
-        block(qb, std::true_type{});
-      else
-        block(qb, std::false_type{});
     }
+    __syncthreads();
   }
 
   if (!wave_live || !kv_ok) return;

@@ -10,9 +10,10 @@
 //   dP^T = V . dO^T
 //   dS^T = P^T * (dP^T - D_i)
 //   dQ^T += K^T . dS^T          (dS feeds the product from registers)
-// and dq = scale * dQ is written in fp32.  K, K^T (bf16 only) and V tiles are
-// staged through LDS with register prefetch; query head h reads kv head
-// h / (H / Hkv) by address.
+// and dq = scale * dQ is written in fp32.  K and V tiles are staged row-major
+// through a double-buffered LDS ring (one barrier per tile); K^T for the last
+// product comes from the same K tile by transpose reads.  Query head h reads kv
+// head h / (H / Hkv) by address.
 #include <type_traits>
 
 #include "attn_device.hpp"
@@ -24,14 +25,10 @@ template <typename T, int HD>
 struct DqCfg {
   static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
   static constexpr int RS = HD + Mma<T>::PADR;
-  static constexpr int TS = BN + 4;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;
   static constexpr int NAS = 32 / Mma<T>::KSTEP;
-  static constexpr bool KT = sizeof(T) == 2;  // bf16 also keeps K transposed in LDS
-  static constexpr int K_ELEMS = BN * RS;
-  static constexpr int KT_ELEMS = KT ? HD * TS : 8;
-  static constexpr int V_ELEMS = BN * RS;
+  static constexpr int TILE = BN * RS;
 };
 
 template <typename T, int HD>
@@ -42,9 +39,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     float c, float scale) {
   using C = DqCfg<T, HD>;
   using M = Mma<T>;
-  __shared__ __align__(16) T sK[C::K_ELEMS];
-  __shared__ __align__(16) T sKt[C::KT_ELEMS];
-  __shared__ __align__(16) T sV[C::V_ELEMS];
+  __shared__ __align__(16) T sK[2][C::TILE];
+  __shared__ __align__(16) T sV[2][C::TILE];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 31, g = lane >> 5;
@@ -93,70 +89,80 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int kv_end = min(S, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
-  TileStage<T, HD, C::BN, C::NT, true, C::KT> stK;
-  TileStage<T, HD, C::BN, C::NT, true, false> stV;
+  TileStage<T, HD, C::BN, C::NT> stK, stV;
   stK.load(kp, 0, S, tid);
   stV.load(vp, 0, S, tid);
+  stK.template store<C::RS>(sK[0], tid);
+  stV.template store<C::RS>(sV[0], tid);
+  if (ntiles > 1) {
+    stK.load(kp, C::BN, S - C::BN, tid);
+    stV.load(vp, C::BN, S - C::BN, tid);
+  }
+  __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
     const int kv_t0 = j * C::BN;
-    __syncthreads();
-    stK.template store<C::RS, C::TS>(sK, sKt, tid);
-    stV.template store<C::RS, C::TS>(sV, nullptr, tid);
-    __syncthreads();
-    if (j + 1 < ntiles) {
-      stK.load(kp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
-      stV.load(vp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
+    if (j + 1 < ntiles) {  // the other buffer was last read before the previous barrier
+      stK.template store<C::RS>(sK[cur ^ 1], tid);
+      stV.template store<C::RS>(sV[cur ^ 1], tid);
+      if (j + 2 < ntiles) {
+        stK.load(kp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
+        stV.load(vp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
+      }
     }
-    if (!wave_live || kv_t0 >= wave_kv_end) continue;
-    // One 32-key block.  Key blocks are 32-aligned like the wave's rows, so a
-    // visited block is either wholly visible or the diagonal block; only the
-    // diagonal block and the sequence tail carry a mask.
-    auto block = [&](const int cb, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      const int kb0 = kv_t0 + 32 * cb;
-      f32x16 s = zero_acc(), dp = zero_acc();
-      const T* krow = sK + (32 * cb + li) * C::RS;
-      const T* vrow = sV + (32 * cb + li) * C::RS;
+    if (wave_live && kv_t0 < wave_kv_end) {
+      const T* tK = sK[cur];
+      const T* tV = sV[cur];
+      // One 32-key block.  Key blocks are 32-aligned like the wave's rows, so a
+      // visited block is either wholly visible or the diagonal block; only the
+      // diagonal block and the sequence tail carry a mask.
+      auto block = [&](const int cb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int kb0 = kv_t0 + 32 * cb;
+        f32x16 s = zero_acc(), dp = zero_acc();
+        const T* krow = tK + (32 * cb + li) * C::RS;
+        const T* vrow = tV + (32 * cb + li) * C::RS;
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        M::mma(s, row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
-        M::mma(dp, row_frag_lds<T, HD>(vrow, g, ks), df[ks]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], c, -lse2));
-        if constexpr (MASK) {
-          const int kv = kb0 + acc_row(r, g);
-          p = (kv <= my_q && kv < S) ? p : 0.f;
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          M::mma(s, row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
+          M::mma(dp, row_frag_lds<T, HD>(vrow, g, ks), df[ks]);
         }
-        s[r] = p * (dp[r] - Drow);  // dS^T
-      }
 #pragma unroll
-      for (int ks = 0; ks < C::NAS; ++ks) {
-        const typename M::frag sf = acc_frag<T>(s, ks * M::KPL);
-#pragma unroll
-        for (int db = 0; db < C::ND; ++db) {
-          const int d = min(32 * db + li, HD - 1);
-          typename M::frag a;
-          if constexpr (C::KT)
-            a = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sKt) + d * C::TS + 32 * cb, g, ks);
-          else
-            a = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sK) + 32 * cb * C::RS, d, g, ks);
-          M::mma(acc[db], a, sf);
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(s[r], c, -lse2));
+          if constexpr (MASK) {
+            const int kv = kb0 + acc_row(r, g);
+            p = (kv <= my_q && kv < S) ? p : 0.f;
+          }
+          s[r] = p * (dp[r] - Drow);  // dS^T
         }
-      }
-    };
+#pragma unroll
+        for (int ks = 0; ks < C::NAS; ++ks) {
+          const typename M::frag sf = acc_frag<T>(s, ks * M::KPL);
+#pragma unroll
+          for (int db = 0; db < C::ND; ++db) {
+            typename M::frag a;
+            if constexpr (sizeof(T) == 2)
+              a = accrow_frag_bf16<HD, C::RS>(tK, 32 * cb + 16 * ks, 32 * db, lane);
+            else
+              a = accrow_frag_f32<C::RS>(tK + 32 * cb * C::RS, min(32 * db + li, HD - 1), g, ks);
+            M::mma(acc[db], a, sf);
+          }
+        }
+      };
 
 #pragma unroll
-    for (int cb = 0; cb < C::NB; ++cb) {
-      const int kb0 = kv_t0 + 32 * cb;
-      if (kb0 >= wave_kv_end) continue;  // wholly above this wave's rows, or past S
-      if (kb0 + 31 > q0 || kb0 + 32 > S)
-        block(cb, std::true_type{});
-      else
-        block(cb, std::false_type{});
+      for (int cb = 0; cb < C::NB; ++cb) {
+        const int kb0 = kv_t0 + 32 * cb;
+        if (kb0 >= wave_kv_end) continue;  // wholly above this wave's rows, or past S
+        if (kb0 + 31 > q0 || kb0 + 32 > S)
+          block(cb, std::true_type{});
+        else
+          block(cb, std::false_type{});
+      }
     }
+    __syncthreads();
   }
 
   if (!wave_live || !q_ok) return;

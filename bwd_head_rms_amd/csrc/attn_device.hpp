@@ -104,17 +104,32 @@ __device__ __forceinline__ typename Mma<T>::frag row_frag_lds(const T* row, int 
 
 // ---------------------------------------------------------------------------
 // Accumulator-row operand: element t of instruction ks for lane group g is tile
-// row acc_row(ks*KPL + t, g) (rows are relative to the 32-row block base), at
-// column `col` of the head dimension.
-//   bf16: read from a transposed LDS tile tt[col][row] (row stride TS): two
-//         runs of four consecutive rows, 8 bytes each.
-//   fp32: read from a row-major LDS tile rt[row][col] (row stride RS).
-template <int TS>
-__device__ __forceinline__ bf16x8 accrow_frag_bf16(const bf16* tt_col, int g, int ks) {
-  const bf16* p = tt_col + 16 * ks + 4 * g;
-  uint2 lo = *reinterpret_cast<const uint2*>(p);
-  uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
-  uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+// row acc_row(ks*KPL + t, g) (rows relative to a 32-row block base), at
+// head-dimension column col0 + l%32 (clamped to the head dimension for hd 16).
+//
+// bf16: read from the row-major LDS tile with ds_read_b64_tr_b16.  Within each
+//   16-lane group that instruction hands lane i element (i mod 4) of the 8 bytes
+//   addressed by lane 4t + floor(i/4), as its element t (t = 0..3).  So lane j of
+//   the group addresses row base + floor(j/4), columns 4*(j mod 4) .. +3, and lane
+//   i receives column i of rows base .. base+3: four consecutive rows of one
+//   column, as the contraction needs.  Two reads give the two runs of four rows
+//   (16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3) of the permuted contraction order.
+//   No transposed copy of the tile is ever stored.
+// fp32: one element per lane, read directly from the row-major tile.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <int HD, int RS>
+__device__ __forceinline__ bf16x8 accrow_frag_bf16(const bf16* tile, int row_base, int col0,
+                                                   int lane) {
+  const int j = lane & 15, G = lane >> 4, g = lane >> 5;
+  const int row = row_base + 4 * g + (j >> 2);
+  const int col = col0 + (HD >= 32 ? 16 * (G & 1) : 0) + 4 * (j & 3);
+  const bf16* p = tile + row * RS + col;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * RS));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 u = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -125,65 +140,43 @@ __device__ __forceinline__ float accrow_frag_f32(const float* rt, int col, int g
 
 // ---------------------------------------------------------------------------
 // Cooperative global -> LDS staging of a ROWS x HD tile, rows [row0, row0+ROWS)
-// of a head plane, zero-filling rows >= nvalid.  Work items are (row pair,
-// 16-byte column chunk); each thread keeps its items in registers between
-// load() and store() so the global loads of the next tile overlap the current
-// tile's arithmetic.  store() writes a row-major copy (row stride RS elements)
-// when ROW is set and, for bf16 when TRANS is set, a transposed copy (column
-// stride TS).
-template <typename T, int HD, int ROWS, int NT, bool ROW, bool TRANS>
+// of a head plane, zero-filling rows >= nvalid.  Work items are 16-byte chunks;
+// each thread keeps its items in registers between load() and store() so the
+// global loads of a later tile overlap the current tile's arithmetic.  store()
+// writes the tile row-major with row stride RS elements.
+template <typename T, int HD, int ROWS, int NT>
 struct TileStage {
   static constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   static constexpr int CPR = HD / EPC;             // chunks per row
-  static constexpr int ITEMS = (ROWS / 2) * CPR;
+  static constexpr int ITEMS = ROWS * CPR;
   static constexpr int PER = (ITEMS + NT - 1) / NT;
-  uint4 buf[PER][2];
+  uint4 buf[PER];
 
   __device__ __forceinline__ void load(const T* plane, int row0, int nvalid, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int item = tid + i * NT;
-      const int p = item / CPR, c = item % CPR;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 2 * p + h;
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if ((ITEMS % NT == 0 || item < ITEMS) && r < nvalid)
-          val = *reinterpret_cast<const uint4*>(plane + (size_t)(row0 + r) * HD + c * EPC);
-        buf[i][h] = val;
-      }
+      const int r = item / CPR, c = item % CPR;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if ((ITEMS % NT == 0 || item < ITEMS) && r < nvalid)
+        val = *reinterpret_cast<const uint4*>(plane + (size_t)(row0 + r) * HD + c * EPC);
+      buf[i] = val;
     }
   }
 
-  template <int RS, int TS>
-  __device__ __forceinline__ void store(T* rowmajor, T* trans, int tid) const {
+  template <int RS>
+  __device__ __forceinline__ void store(T* tile, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int item = tid + i * NT;
       if (ITEMS % NT != 0 && item >= ITEMS) continue;
-      const int p = item / CPR, c = item % CPR;
+      const int r = item / CPR, c = item % CPR;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint4*>(tile + r * RS + c * EPC) = buf[i];
+      } else {
+        const float* f = reinterpret_cast<const float*>(&buf[i]);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 2 * p + h;
-        if constexpr (!ROW) {
-        } else if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<uint4*>(rowmajor + r * RS + c * EPC) = buf[i][h];
-        } else {
-          const float* f = reinterpret_cast<const float*>(&buf[i][h]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rowmajor[r * RS + c * EPC + e] = f[e];
-        }
-      }
-      if constexpr (TRANS && sizeof(T) == 2) {
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&buf[i][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&buf[i][1]);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const uint32_t a = w0[t >> 1], b = w1[t >> 1];
-          const uint32_t pair = (t & 1) ? ((a >> 16) | (b & 0xFFFF0000u))
-                                        : ((a & 0xFFFFu) | (b << 16));
-          *reinterpret_cast<uint32_t*>(trans + (c * EPC + t) * TS + 2 * p) = pair;
-        }
+        for (int e = 0; e < 4; ++e) tile[r * RS + c * EPC + e] = f[e];
       }
     }
   }

@@ -1,8 +1,9 @@
 // attn_fwd.hip -- fused causal attention forward for gfx950.
 //
 // One workgroup (4 waves) per (batch, head, 128-row query tile); each wave owns
-// 32 query rows.  Key/value tiles of 64 rows are staged through LDS (register
-// prefetch of the next tile overlaps the current tile's arithmetic) and shared
+// 32 query rows.  Key/value tiles of 64 rows are staged row-major through a
+// double-buffered LDS ring (the global loads of tile j+2 and the LDS store of
+// tile j+1 overlap the arithmetic on tile j; one barrier per tile) and shared
 // by the four waves.  Per tile and wave:
 //   S^T = K . Q^T            (MFMA; keys are rows, queries are lanes, so every
 //                              softmax row lives in one lane pair)
@@ -11,7 +12,8 @@
 //   exp2(m_old - m_new) when a row's max grows past its slack (the online
 //   softmax of the fused kernel in the "xtrain evolution overview", infra
 //   table row T14)
-//   O^T += V^T . P^T          (MFMA; P feeds the product from registers)
+//   O^T += V^T . P^T          (MFMA; P feeds the product from registers, V^T
+//                              comes from the row-major tile by transpose reads)
 // Tiles wholly above the diagonal are never visited; blocks of 32 keys wholly
 // above a wave's rows are skipped; the mask is applied only on the diagonal
 // block and at the end of the sequence.  The epilogue writes O and the
@@ -31,14 +33,11 @@ constexpr float kRescaleSlack = 8.f;
 template <typename T, int HD>
 struct FwdCfg {
   static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
-  static constexpr int RS = HD + Mma<T>::PADR;  // row-major LDS row stride
-  static constexpr int TS = BN + 4;             // transposed LDS row stride
+  static constexpr int RS = HD + Mma<T>::PADR;    // LDS row stride (elements)
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;  // head-dim contraction steps
   static constexpr int NAS = 32 / Mma<T>::KSTEP;  // key contraction steps per 32-key block
-  static constexpr bool VT = sizeof(T) == 2;      // bf16 keeps V transposed in LDS
-  static constexpr int K_ELEMS = BN * RS;
-  static constexpr int V_ELEMS = VT ? HD * TS : BN * RS;
+  static constexpr int TILE = BN * RS;
 };
 
 template <typename T, int HD>
@@ -47,8 +46,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     T* __restrict__ o, float* __restrict__ lse, int S, int H, int Hkv, int nqt, int BH, float c) {
   using C = FwdCfg<T, HD>;
   using M = Mma<T>;
-  __shared__ __align__(16) T sK[C::K_ELEMS];
-  __shared__ __align__(16) T sV[C::V_ELEMS];
+  __shared__ __align__(16) T sK[2][C::TILE];
+  __shared__ __align__(16) T sV[2][C::TILE];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 31, g = lane >> 5;
@@ -80,93 +79,102 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   const int kv_end = min(S, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
-  TileStage<T, HD, C::BN, C::NT, true, false> stK;
-  TileStage<T, HD, C::BN, C::NT, !C::VT, C::VT> stV;
+  TileStage<T, HD, C::BN, C::NT> stK, stV;
   stK.load(kp, 0, S, tid);
   stV.load(vp, 0, S, tid);
+  stK.template store<C::RS>(sK[0], tid);
+  stV.template store<C::RS>(sV[0], tid);
+  if (ntiles > 1) {
+    stK.load(kp, C::BN, S - C::BN, tid);
+    stV.load(vp, C::BN, S - C::BN, tid);
+  }
+  __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
+    const int cur = j & 1;
     const int kv_t0 = j * C::BN;
-    __syncthreads();
-    stK.template store<C::RS, C::TS>(sK, nullptr, tid);
-    stV.template store<C::RS, C::TS>(sV, sV, tid);
-    __syncthreads();
-    if (j + 1 < ntiles) {
-      stK.load(kp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
-      stV.load(vp, kv_t0 + C::BN, S - kv_t0 - C::BN, tid);
+    if (j + 1 < ntiles) {  // the other buffer was last read before the previous barrier
+      stK.template store<C::RS>(sK[cur ^ 1], tid);
+      stV.template store<C::RS>(sV[cur ^ 1], tid);
+      if (j + 2 < ntiles) {
+        stK.load(kp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
+        stV.load(vp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
+      }
     }
-    if (!wave_live || kv_t0 >= wave_kv_end) continue;
-
-    // Scores of the (up to) two 32-key blocks of this tile.  Key blocks are
-    // 32-aligned like the wave's rows: a visited block is wholly visible or the
-    // diagonal block, and only the diagonal block and the sequence tail carry a
-    // mask (masked scores become -inf, i.e. weight exactly 0).
-    f32x16 s[C::NB];
-    bool act[C::NB];
+    if (wave_live && kv_t0 < wave_kv_end) {
+      const T* tK = sK[cur];
+      const T* tV = sV[cur];
+      // Scores of the (up to) two 32-key blocks of this tile.  Key blocks are
+      // 32-aligned like the wave's rows: a visited block is wholly visible or
+      // the diagonal block, and only the diagonal block and the sequence tail
+      // carry a mask (masked scores become -inf, i.e. weight exactly 0).
+      f32x16 s[C::NB];
+      bool act[C::NB];
 #pragma unroll
-    for (int cb = 0; cb < C::NB; ++cb) {
-      const int kb0 = kv_t0 + 32 * cb;
-      act[cb] = kb0 < wave_kv_end;
-      s[cb] = zero_acc();
-      if (act[cb]) {
-        const T* krow = sK + (32 * cb + li) * C::RS;
+      for (int cb = 0; cb < C::NB; ++cb) {
+        const int kb0 = kv_t0 + 32 * cb;
+        act[cb] = kb0 < wave_kv_end;
+        s[cb] = zero_acc();
+        if (act[cb]) {
+          const T* krow = tK + (32 * cb + li) * C::RS;
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) M::mma(s[cb], row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
-        if (kb0 + 31 > q0 || kb0 + 32 > S) {
+          for (int ks = 0; ks < C::NKS; ++ks) M::mma(s[cb], row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
+          if (kb0 + 31 > q0 || kb0 + 32 > S) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kv = kb0 + acc_row(r, g);
-            s[cb][r] = (kv <= my_q && kv < S) ? s[cb][r] : -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+              const int kv = kb0 + acc_row(r, g);
+              s[cb][r] = (kv <= my_q && kv < S) ? s[cb][r] : -INFINITY;
+            }
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < C::NB; ++cb)
+        if (act[cb]) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      // Lazy rescale: a row keeps its reference max m while its scores stay
+      // below m + kRescaleSlack (log2 units), so P <= 2^kRescaleSlack and the
+      // accumulator is rescaled only when some row's max really grows.  The
+      // decision is per row (rows that do not need it multiply by exactly 1),
+      // so every row's result depends only on that row's scores.
+      const bool grow = mx > m + kRescaleSlack;
+      if (__ballot(grow)) {
+        const float m_new = grow ? mx : m;
+        const float alpha = grow ? fast_exp2(m - m_new) : 1.f;
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
+      }
+#pragma unroll
+      for (int cb = 0; cb < C::NB; ++cb) {
+        if (!act[cb]) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[cb][r], c, -m));
+          s[cb][r] = p;
+          l += p;
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::NAS; ++ks) {
+          const typename M::frag pf = acc_frag<T>(s[cb], ks * M::KPL);
+#pragma unroll
+          for (int db = 0; db < C::ND; ++db) {
+            typename M::frag a;
+            if constexpr (sizeof(T) == 2)
+              a = accrow_frag_bf16<HD, C::RS>(tV, 32 * cb + 16 * ks, 32 * db, lane);
+            else
+              a = accrow_frag_f32<C::RS>(tV + 32 * cb * C::RS, min(32 * db + li, HD - 1), g, ks);
+            M::mma(oacc[db], a, pf);
           }
         }
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int cb = 0; cb < C::NB; ++cb)
-      if (act[cb]) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-    // Lazy rescale: a row keeps its reference max m while its scores stay
-    // below m + kRescaleSlack (log2 units), so P <= 2^kRescaleSlack and the
-    // accumulator is rescaled only when some row's max really grows.  The
-    // decision is per row (rows that do not need it multiply by exactly 1),
-    // so every row's result depends only on that row's scores.
-    const bool grow = mx > m + kRescaleSlack;
-    if (__ballot(grow)) {
-      const float m_new = grow ? mx : m;
-      const float alpha = grow ? fast_exp2(m - m_new) : 1.f;
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
-    }
-#pragma unroll
-    for (int cb = 0; cb < C::NB; ++cb) {
-      if (!act[cb]) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[cb][r], c, -m));
-        s[cb][r] = p;
-        l += p;
-      }
-#pragma unroll
-      for (int ks = 0; ks < C::NAS; ++ks) {
-        const typename M::frag pf = acc_frag<T>(s[cb], ks * M::KPL);
-#pragma unroll
-        for (int db = 0; db < C::ND; ++db) {
-          const int d = min(32 * db + li, HD - 1);
-          typename M::frag a;
-          if constexpr (C::VT)
-            a = accrow_frag_bf16<C::TS>(reinterpret_cast<const bf16*>(sV) + d * C::TS + 32 * cb, g, ks);
-          else
-            a = accrow_frag_f32<C::RS>(reinterpret_cast<const float*>(sV) + 32 * cb * C::RS, d, g, ks);
-          M::mma(oacc[db], a, pf);
-        }
-      }
-    }
+    __syncthreads();
   }
 
   if (!wave_live) return;
