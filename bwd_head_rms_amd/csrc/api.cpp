@@ -62,7 +62,7 @@ int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, 
 size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype) {
   if (dtype != XATTN_F32 && dtype != XATTN_BF16) return 0;
   if (check_shape(B, S, H, Hkv, hd) != XATTN_OK) return 0;
-  return sizeof(float) * (size_t)B * (size_t)H * (size_t)S;
+  return 2 * sizeof(float) * (size_t)B * (size_t)H * (size_t)S;  // D and LSE*log2e per row
 }
 
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,

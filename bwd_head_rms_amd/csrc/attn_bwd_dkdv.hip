@@ -4,9 +4,9 @@
 // 32 key rows whose K and V operands stay in registers for the whole kernel.
 // The workgroup walks every query head of its GQA group (r ascending) and, for
 // each, the query tiles (128 rows for bf16, 64 for fp32) at or below the
-// diagonal (ascending), staging Q, dO, LSE and D row-major through a
-// double-buffered LDS ring (one barrier per tile).  Per 32-row query block and
-// wave:
+// diagonal (ascending), copying Q and dO (bf16: asynchronously, straight from
+// HBM into swizzled tiles), LSE and D into a double-buffered LDS ring (one
+// barrier per tile).  Per 32-row query block and wave:
 //   S  = Q . K^T,   P = exp2(S*scale*log2e - LSE_i*log2e)     (recompute)
 //   dP = dO . V^T,  dS = P * (dP - D_i)
 //   dV^T += dO^T . P          (P feeds the product from registers; dO^T and
@@ -30,19 +30,18 @@ struct DkvCfg {
   static constexpr int NW = 4, NT = NW * kWave, BN = 32 * NW;
   static constexpr int BMQ = sizeof(T) == 2 ? 128 : 64;  // query rows per staged tile
   static constexpr int NQB = BMQ / 32;
-  static constexpr int RS = HD + Mma<T>::PADR;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;
   static constexpr int NAS = 32 / Mma<T>::KSTEP;
-  static constexpr int TILE = BMQ * RS;
+  static constexpr int TILE = Tile<T, HD, BMQ>::ELEMS;
 };
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ dws,
-    float* __restrict__ dk, float* __restrict__ dv, int S, int H, int Hkv, int nkt, int BG,
-    float c, float scale) {
+    float* __restrict__ dk, float* __restrict__ dv, int B, int S, int H, int Hkv, int nkt,
+    int BG, float c, float scale) {
   using C = DkvCfg<T, HD>;
   using M = Mma<T>;
   __shared__ __align__(16) T sQ[2][C::TILE];
@@ -83,40 +82,41 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int per_head = nq - qt_first;
   const int iters = group * per_head;
 
-  TileStage<T, HD, C::BMQ, C::NT> stQ, stO;
-  float pre_l = 0.f, pre_d = 0.f;
-  auto prefetch = [&](int it) {
+  wait_global_loads();  // the key / value operands above are in registers
+  Stager<T, HD, C::BMQ, C::NW> stQ, stO;
+  const float* lse2 = dws + (size_t)B * H * S;  // LSE*log2e, written by the dq kernel
+  // issue the copies of tile `it` (Q, dO, LSE*log2e, D) into buffer `buf`
+  auto issue = [&](int it, int buf) {
     const int r = it / per_head, qt = qt_first + it % per_head;
     const size_t bh = (size_t)b * H + (size_t)kvh * group + r;
     const int row0 = qt * C::BMQ;
-    stQ.load(q + bh * S * HD, row0, S - row0, tid);
-    stO.load(dO + bh * S * HD, row0, S - row0, tid);
-    if (tid < C::BMQ) {
-      const int qi = row0 + tid;
-      pre_l = qi < S ? lse[bh * S + qi] * kLog2e : 0.f;
-      pre_d = qi < S ? dws[bh * S + qi] : 0.f;
+    stQ.issue(q + bh * S * HD, row0, S, sQ[buf], wave, lane, tid);
+    stO.issue(dO + bh * S * HD, row0, S, sO[buf], wave, lane, tid);
+    // per-row statistics: 64 rows per wave instruction, rows past S read row S-1
+    constexpr int NST = C::BMQ / kWave;
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      if (wave == i) {
+        const int qi = min(row0 + kWave * i + lane, S - 1);
+        lds_copy4(lse2 + bh * S + qi, &sL[buf][kWave * i]);
+        lds_copy4(dws + bh * S + qi, &sD[buf][kWave * i]);
+      }
     }
   };
-  auto stage = [&](int buf) {
-    stQ.template store<C::RS>(sQ[buf], tid);
-    stO.template store<C::RS>(sO[buf], tid);
-    if (tid < C::BMQ) {
-      sL[buf][tid] = pre_l;
-      sD[buf][tid] = pre_d;
-    }
+  auto commit = [&](int buf) {
+    wait_global_loads();
+    stQ.commit(sQ[buf], tid);
+    stO.commit(sO[buf], tid);
   };
-  prefetch(0);
-  stage(0);
-  if (iters > 1) prefetch(1);
+  issue(0, 0);
+  commit(0);
   __syncthreads();
 
   for (int it = 0; it < iters; ++it) {
     const int cur = it & 1;
     const int qt = qt_first + it % per_head;
-    if (it + 1 < iters) {  // the other buffer was last read before the previous barrier
-      stage(cur ^ 1);
-      if (it + 2 < iters) prefetch(it + 2);
-    }
+    const bool more = it + 1 < iters;
+    if (more) issue(it + 1, cur ^ 1);  // the other buffer was last read before the previous barrier
     if (wave_live) {
       const T* tQ = sQ[cur];
       const T* tO = sO[cur];
@@ -129,12 +129,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         constexpr bool MASK = decltype(mask_tag)::value;
         const int qb0 = qt * C::BMQ + 32 * qb;
         f32x16 s = zero_acc(), dp = zero_acc();
-        const T* qrow = tQ + (32 * qb + li) * C::RS;
-        const T* orow = tO + (32 * qb + li) * C::RS;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          M::mma(s, row_frag_lds<T, HD>(qrow, g, ks), kf[ks]);
-          M::mma(dp, row_frag_lds<T, HD>(orow, g, ks), vf[ks]);
+          M::mma(s, row_frag_lds<T, HD, C::BMQ>(tQ, 32 * qb + li, g, ks), kf[ks]);
+          M::mma(dp, row_frag_lds<T, HD, C::BMQ>(tO, 32 * qb + li, g, ks), vf[ks]);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -153,17 +151,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           const typename M::frag sf = acc_frag<T>(dp, ks * M::KPL);
 #pragma unroll
           for (int db = 0; db < C::ND; ++db) {
-            typename M::frag ao, aq;
-            if constexpr (sizeof(T) == 2) {
-              ao = accrow_frag_bf16<HD, C::RS>(tO, 32 * qb + 16 * ks, 32 * db, lane);
-              aq = accrow_frag_bf16<HD, C::RS>(tQ, 32 * qb + 16 * ks, 32 * db, lane);
-            } else {
-              const int d = min(32 * db + li, HD - 1);
-              ao = accrow_frag_f32<C::RS>(tO + 32 * qb * C::RS, d, g, ks);
-              aq = accrow_frag_f32<C::RS>(tQ + 32 * qb * C::RS, d, g, ks);
-            }
-            M::mma(dvacc[db], ao, pf);
-            M::mma(dkacc[db], aq, sf);
+            M::mma(dvacc[db], accrow_frag<T, HD, C::BMQ>(tO, 32 * qb, ks, 32 * db, lane), pf);
+            M::mma(dkacc[db], accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane), sf);
           }
         }
       };
@@ -185,6 +174,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         }
       }
     }
+    if (more) commit(cur ^ 1);
     __syncthreads();
   }
 
@@ -214,8 +204,8 @@ static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* 
   const int BG = d.B * d.Hkv;
   dim3 grid((unsigned)(nkt * BG)), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
-                     (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, d.S, d.H, d.Hkv,
-                     nkt, BG, scale * kLog2e, scale);
+                     (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, d.B, d.S, d.H,
+                     d.Hkv, nkt, BG, scale * kLog2e, scale);
 }
 
 void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,

@@ -10,9 +10,11 @@
 //   dP^T = V . dO^T
 //   dS^T = P^T * (dP^T - D_i)
 //   dQ^T += K^T . dS^T          (dS feeds the product from registers)
-// and dq = scale * dQ is written in fp32.  K and V tiles are staged row-major
-// through a double-buffered LDS ring (one barrier per tile); K^T for the last
-// product comes from the same K tile by transpose reads.  Query head h reads kv
+// and dq = scale * dQ is written in fp32.  The workspace receives D and
+// LSE*log2e per row ([2][B][H][S] floats) for the dK/dV kernel.  K and V tiles are copied into a
+// double-buffered LDS ring (bf16: asynchronously, straight from HBM; one
+// barrier per tile); K^T for the last product comes from the same K tile by
+// transpose reads.  Query head h reads kv
 // head h / (H / Hkv) by address.
 #include <type_traits>
 
@@ -24,11 +26,10 @@ namespace xattn {
 template <typename T, int HD>
 struct DqCfg {
   static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
-  static constexpr int RS = HD + Mma<T>::PADR;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;
   static constexpr int NAS = 32 / Mma<T>::KSTEP;
-  static constexpr int TILE = BN * RS;
+  static constexpr int TILE = Tile<T, HD, BN>::ELEMS;
 };
 
 template <typename T, int HD>
@@ -79,8 +80,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     }
   }
   const float Drow = Dp + __shfl_xor(Dp, 32);
-  if (q_ok && g == 0) dws[(size_t)bh * S + my_q] = Drow;
   const float lse2 = q_ok ? lse[(size_t)bh * S + my_q] * kLog2e : 0.f;
+  if (q_ok && g == 0) {
+    dws[(size_t)bh * S + my_q] = Drow;
+    dws[(size_t)BH * S + (size_t)bh * S + my_q] = lse2;  // for the dk/dv kernel
+  }
 
   f32x16 acc[C::ND];
 #pragma unroll
@@ -89,27 +93,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int kv_end = min(S, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
-  TileStage<T, HD, C::BN, C::NT> stK, stV;
-  stK.load(kp, 0, S, tid);
-  stV.load(vp, 0, S, tid);
-  stK.template store<C::RS>(sK[0], tid);
-  stV.template store<C::RS>(sV[0], tid);
-  if (ntiles > 1) {
-    stK.load(kp, C::BN, S - C::BN, tid);
-    stV.load(vp, C::BN, S - C::BN, tid);
-  }
+  wait_global_loads();  // the per-row operands above are in registers
+  Stager<T, HD, C::BN, C::NW> stK, stV;
+  stK.issue(kp, 0, S, sK[0], wave, lane, tid);
+  stV.issue(vp, 0, S, sV[0], wave, lane, tid);
+  wait_global_loads();
+  stK.commit(sK[0], tid);
+  stV.commit(sV[0], tid);
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     const int cur = j & 1;
     const int kv_t0 = j * C::BN;
-    if (j + 1 < ntiles) {  // the other buffer was last read before the previous barrier
-      stK.template store<C::RS>(sK[cur ^ 1], tid);
-      stV.template store<C::RS>(sV[cur ^ 1], tid);
-      if (j + 2 < ntiles) {
-        stK.load(kp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
-        stV.load(vp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
-      }
+    const bool more = j + 1 < ntiles;
+    if (more) {  // the other buffer was last read before the previous barrier
+      stK.issue(kp, kv_t0 + C::BN, S, sK[cur ^ 1], wave, lane, tid);
+      stV.issue(vp, kv_t0 + C::BN, S, sV[cur ^ 1], wave, lane, tid);
     }
     if (wave_live && kv_t0 < wave_kv_end) {
       const T* tK = sK[cur];
@@ -121,12 +120,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         constexpr bool MASK = decltype(mask_tag)::value;
         const int kb0 = kv_t0 + 32 * cb;
         f32x16 s = zero_acc(), dp = zero_acc();
-        const T* krow = tK + (32 * cb + li) * C::RS;
-        const T* vrow = tV + (32 * cb + li) * C::RS;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          M::mma(s, row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
-          M::mma(dp, row_frag_lds<T, HD>(vrow, g, ks), df[ks]);
+          M::mma(s, row_frag_lds<T, HD, C::BN>(tK, 32 * cb + li, g, ks), qf[ks]);
+          M::mma(dp, row_frag_lds<T, HD, C::BN>(tV, 32 * cb + li, g, ks), df[ks]);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -142,12 +139,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
           const typename M::frag sf = acc_frag<T>(s, ks * M::KPL);
 #pragma unroll
           for (int db = 0; db < C::ND; ++db) {
-            typename M::frag a;
-            if constexpr (sizeof(T) == 2)
-              a = accrow_frag_bf16<HD, C::RS>(tK, 32 * cb + 16 * ks, 32 * db, lane);
-            else
-              a = accrow_frag_f32<C::RS>(tK + 32 * cb * C::RS, min(32 * db + li, HD - 1), g, ks);
-            M::mma(acc[db], a, sf);
+            M::mma(acc[db], accrow_frag<T, HD, C::BN>(tK, 32 * cb, ks, 32 * db, lane), sf);
           }
         }
       };
@@ -161,6 +153,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         else
           block(cb, std::false_type{});
       }
+    }
+    if (more) {
+      wait_global_loads();
+      stK.commit(sK[cur ^ 1], tid);
+      stV.commit(sV[cur ^ 1], tid);
     }
     __syncthreads();
   }

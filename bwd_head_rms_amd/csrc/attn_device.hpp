@@ -91,96 +91,196 @@ __device__ __forceinline__ typename Mma<T>::frag row_frag_global(const T* row, i
   }
 }
 
-// Same, from a row-major LDS tile.
-template <typename T, int HD>
-__device__ __forceinline__ typename Mma<T>::frag row_frag_lds(const T* row, int g, int ks) {
-  if constexpr (sizeof(T) == 2) {
-    uint4 u = *reinterpret_cast<const uint4*>(row + g * (HD / 2) + ks * 8);
-    return __builtin_bit_cast(bf16x8, u);
-  } else {
-    return row[g * (HD / 2) + ks];
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Accumulator-row operand: element t of instruction ks for lane group g is tile
-// row acc_row(ks*KPL + t, g) (rows relative to a 32-row block base), at
-// head-dimension column col0 + l%32 (clamped to the head dimension for hd 16).
+// LDS tiles of ROWS x HD elements.
 //
-// bf16: read from the row-major LDS tile with ds_read_b64_tr_b16.  Within each
-//   16-lane group that instruction hands lane i element (i mod 4) of the 8 bytes
-//   addressed by lane 4t + floor(i/4), as its element t (t = 0..3).  So lane j of
-//   the group addresses row base + floor(j/4), columns 4*(j mod 4) .. +3, and lane
-//   i receives column i of rows base .. base+3: four consecutive rows of one
-//   column, as the contraction needs.  Two reads give the two runs of four rows
-//   (16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3) of the permuted contraction order.
-//   No transposed copy of the tile is ever stored.
-// fp32: one element per lane, read directly from the row-major tile.
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-template <int HD, int RS>
-__device__ __forceinline__ bf16x8 accrow_frag_bf16(const bf16* tile, int row_base, int col0,
-                                                   int lane) {
-  const int j = lane & 15, G = lane >> 4, g = lane >> 5;
-  const int row = row_base + 4 * g + (j >> 2);
-  const int col = col0 + (HD >= 32 ? 16 * (G & 1) : 0) + 4 * (j & 3);
-  const bf16* p = tile + row * RS + col;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 8 * RS));
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
-  const v8i16 u = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, u);
+// bf16: rows of HD elements with no padding, filled by global_load_lds_dwordx4
+//   (each lane's 16 bytes land at the instruction's LDS base + 16 * lane, so a
+//   wave instruction writes 1 KB of consecutive rows and no per-row padding is
+//   possible).  Instead the 16-byte chunks of each row are XOR-swizzled by row:
+//   logical chunk c of row r lives at physical chunk c ^ swz(r).  swz is chosen
+//   (for 64 banks of 4 bytes) so that both read patterns are conflict free: 16
+//   lanes reading one chunk of 16 consecutive rows, and the transpose reads
+//   (4 consecutive rows x 4 consecutive chunks per half wave).  Rows past the
+//   sequence end are loaded from row S-1 (finite data; the mask removes them).
+// fp32: rows padded to HD+1 elements (odd stride), staged through registers.
+// One wave instruction copying 16 bytes per lane from global memory into LDS:
+// lane l's bytes land at lds_dst + 16*l (global_load_lds_dwordx4, base in M0).
+// Written as inline assembly so that the compiler does not treat the copy in
+// flight into one buffer as a hazard for reads of the other buffer (it would
+// otherwise wait for the copy before every LDS read); completion is awaited
+// explicitly (wait_global_loads) before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_copy16(const void* src, const void* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
 }
 
-template <int RS>
-__device__ __forceinline__ float accrow_frag_f32(const float* rt, int col, int g, int ks) {
-  return rt[acc_row(ks, g) * RS + col];
+// Same with 4 bytes per lane (global_load_lds_dword): lane l's dword lands at
+// lds_dst + 4*l.
+__device__ __forceinline__ void lds_copy4(const void* src, const void* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
 }
 
-// ---------------------------------------------------------------------------
-// Cooperative global -> LDS staging of a ROWS x HD tile, rows [row0, row0+ROWS)
-// of a head plane, zero-filling rows >= nvalid.  Work items are 16-byte chunks;
-// each thread keeps its items in registers between load() and store() so the
-// global loads of a later tile overlap the current tile's arithmetic.  store()
-// writes the tile row-major with row stride RS elements.
-template <typename T, int HD, int ROWS, int NT>
-struct TileStage {
-  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  static constexpr int CPR = HD / EPC;             // chunks per row
+template <typename T, int HD, int ROWS>
+struct Tile;
+
+template <int HD, int ROWS>
+struct Tile<bf16, HD, ROWS> {
+  static constexpr int CPR = HD / 8;          // 16-byte chunks per row
+  static constexpr int ELEMS = ROWS * HD;
+  static constexpr int ROWS_PER_INST = 64 / CPR;
+  static constexpr int NINST = ROWS / ROWS_PER_INST;
+  static_assert(ROWS % ROWS_PER_INST == 0, "tile rows must fill whole wave loads");
+
+  __device__ static constexpr int swz(int r) {
+    if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else if constexpr (CPR == 4) return (r >> 2) & 3;
+    else return (r >> 3) & 1;
+  }
+  // Element offset of (row r, column col); valid for accesses inside one chunk.
+  __device__ static int off(int r, int col) {
+    return r * HD + ((((col >> 3) ^ swz(r))) << 3) + (col & 7);
+  }
+  // Issue the asynchronous copy of rows [row0, row0 + ROWS) of a head plane
+  // (row stride HD) into `tile`, shared by NW waves.  Completion is tracked by
+  // vmcnt: wait for it before the barrier that publishes the tile.
+  template <int NW>
+  __device__ static void issue(const bf16* plane, int row0, int S, bf16* tile, int wave, int lane) {
+#pragma unroll
+    for (int i = wave; i < NINST; i += NW) {
+      const int r = i * ROWS_PER_INST + lane / CPR;
+      const int chunk = (lane % CPR) ^ swz(r);
+      const int gr = min(row0 + r, S - 1);
+      lds_copy16(plane + (size_t)gr * HD + chunk * 8, tile + i * 512);
+    }
+  }
+};
+
+template <int HD, int ROWS>
+struct Tile<float, HD, ROWS> {
+  static constexpr int RS = HD + 1;
+  static constexpr int ELEMS = ROWS * RS;
+  __device__ static int off(int r, int col) { return r * RS + col; }
+};
+
+// Register staging of an fp32 tile: load() issues the global loads (rows past
+// the sequence end read as zero), store() writes them to LDS.
+template <int HD, int ROWS, int NT>
+struct F32Stage {
+  static constexpr int CPR = HD / 4;
   static constexpr int ITEMS = ROWS * CPR;
   static constexpr int PER = (ITEMS + NT - 1) / NT;
-  uint4 buf[PER];
+  float4 buf[PER];
 
-  __device__ __forceinline__ void load(const T* plane, int row0, int nvalid, int tid) {
+  __device__ __forceinline__ void load(const float* plane, int row0, int S, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int item = tid + i * NT;
       const int r = item / CPR, c = item % CPR;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if ((ITEMS % NT == 0 || item < ITEMS) && r < nvalid)
-        val = *reinterpret_cast<const uint4*>(plane + (size_t)(row0 + r) * HD + c * EPC);
+      float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+      if ((ITEMS % NT == 0 || item < ITEMS) && row0 + r < S)
+        val = *reinterpret_cast<const float4*>(plane + (size_t)(row0 + r) * HD + c * 4);
       buf[i] = val;
     }
   }
-
-  template <int RS>
-  __device__ __forceinline__ void store(T* tile, int tid) const {
+  __device__ __forceinline__ void store(float* tile, int tid) const {
+    constexpr int RS = Tile<float, HD, ROWS>::RS;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int item = tid + i * NT;
       if (ITEMS % NT != 0 && item >= ITEMS) continue;
       const int r = item / CPR, c = item % CPR;
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<uint4*>(tile + r * RS + c * EPC) = buf[i];
-      } else {
-        const float* f = reinterpret_cast<const float*>(&buf[i]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) tile[r * RS + c * EPC + e] = f[e];
-      }
+      tile[r * RS + c * 4 + 0] = buf[i].x;
+      tile[r * RS + c * 4 + 1] = buf[i].y;
+      tile[r * RS + c * 4 + 2] = buf[i].z;
+      tile[r * RS + c * 4 + 3] = buf[i].w;
     }
   }
 };
+
+// Double-buffered staging of one tensor's tiles: issue(next) before the
+// arithmetic on the current tile, commit(next) after it; a barrier follows.
+// bf16 copies asynchronously straight into LDS; fp32 goes through registers.
+template <typename T, int HD, int ROWS, int NW>
+struct Stager {
+  using TL = Tile<T, HD, ROWS>;
+  F32Stage<HD, ROWS, NW * kWave> regs;  // unused for bf16
+  __device__ __forceinline__ void issue(const T* plane, int row0, int S, T* tile, int wave,
+                                        int lane, int tid) {
+    if constexpr (sizeof(T) == 2)
+      TL::template issue<NW>(plane, row0, S, tile, wave, lane);
+    else
+      regs.load(plane, row0, S, tid);
+  }
+  __device__ __forceinline__ void commit(T* tile, int tid) const {
+    if constexpr (sizeof(T) == 4) regs.store(tile, tid);
+  }
+};
+
+// Wait for all of this wave's outstanding global loads, including copies into
+// LDS.  The wait is the compiler's own s_waitcnt (vmcnt(0); expcnt and lgkmcnt
+// left at their maximum, gfx9 encoding), so the compiler also knows that no
+// load is pending afterwards and adds no waits of its own later; the empty asm
+// keeps memory accesses from moving across it.
+__device__ __forceinline__ void wait_global_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  asm volatile("" ::: "memory");
+}
+
+// Head-dimension operand of tile row r (elements d = g*HD/2 + ks*KPL + t).
+template <typename T, int HD, int ROWS>
+__device__ __forceinline__ typename Mma<T>::frag row_frag_lds(const T* tile, int r, int g, int ks) {
+  using TL = Tile<T, HD, ROWS>;
+  if constexpr (sizeof(T) == 2) {
+    const uint4 u = *reinterpret_cast<const uint4*>(tile + TL::off(r, g * (HD / 2) + ks * 8));
+    return __builtin_bit_cast(bf16x8, u);
+  } else {
+    return tile[TL::off(r, g * (HD / 2) + ks)];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Accumulator-row operand of instruction ks for a 32-row block starting at tile
+// row `base`: element t for lane group g is tile row base + acc_row(ks*KPL+t, g),
+// at head-dimension column col0 + l%32 (duplicated for hd 16).
+//
+// bf16: ds_read_b64_tr_b16.  Within each 16-lane group that instruction hands
+//   lane i element (i mod 4) of the 8 bytes addressed by lane 4t + floor(i/4),
+//   as its element t (t = 0..3).  So lane j of the group addresses row
+//   base' + floor(j/4), columns 4*(j mod 4) .. +3, and lane i receives column i
+//   of rows base' .. base'+3: four consecutive rows of one column, as the
+//   contraction needs.  Two reads give the two runs of four rows
+//   (16ks + 4g + 0..3 and 16ks + 8 + 4g + 0..3) of the permuted contraction
+//   order.  No transposed copy of a tile is ever stored.
+// fp32: one element per lane, read directly.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+template <typename T, int HD, int ROWS>
+__device__ __forceinline__ typename Mma<T>::frag accrow_frag(const T* tile, int base, int ks,
+                                                              int col0, int lane) {
+  using TL = Tile<T, HD, ROWS>;
+  const int g = lane >> 5;
+  if constexpr (sizeof(T) == 2) {
+    const int j = lane & 15, G = lane >> 4;
+    const int row = base + 16 * ks + 4 * g + (j >> 2);
+    const int col = col0 + (HD >= 32 ? 16 * (G & 1) : 0) + 4 * (j & 3);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + TL::off(row, col)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + TL::off(row + 8, col)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 u = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, u);
+  } else {
+    return tile[TL::off(base + acc_row(ks, g), min(col0 + (lane & 31), HD - 1))];
+  }
+}
 
 template <typename T>
 __device__ __forceinline__ typename Mma<T>::frag zero_frag() {

@@ -1,10 +1,10 @@
 // attn_fwd.hip -- fused causal attention forward for gfx950.
 //
 // One workgroup (4 waves) per (batch, head, 128-row query tile); each wave owns
-// 32 query rows.  Key/value tiles of 64 rows are staged row-major through a
-// double-buffered LDS ring (the global loads of tile j+2 and the LDS store of
-// tile j+1 overlap the arithmetic on tile j; one barrier per tile) and shared
-// by the four waves.  Per tile and wave:
+// 32 query rows.  Key/value tiles of 64 rows are copied into a double-buffered
+// LDS ring (bf16: asynchronously, straight from HBM into swizzled tiles; the
+// copy of tile j+1 overlaps the arithmetic on tile j; one barrier per tile) and
+// shared by the four waves.  Per tile and wave:
 //   S^T = K . Q^T            (MFMA; keys are rows, queries are lanes, so every
 //                              softmax row lives in one lane pair)
 //   online softmax in the log2 domain: reference max m and sum l per query,
@@ -33,11 +33,10 @@ constexpr float kRescaleSlack = 8.f;
 template <typename T, int HD>
 struct FwdCfg {
   static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
-  static constexpr int RS = HD + Mma<T>::PADR;    // LDS row stride (elements)
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;  // head-dim contraction steps
   static constexpr int NAS = 32 / Mma<T>::KSTEP;  // key contraction steps per 32-key block
-  static constexpr int TILE = BN * RS;
+  static constexpr int TILE = Tile<T, HD, BN>::ELEMS;
 };
 
 template <typename T, int HD>
@@ -79,27 +78,22 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   const int kv_end = min(S, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
-  TileStage<T, HD, C::BN, C::NT> stK, stV;
-  stK.load(kp, 0, S, tid);
-  stV.load(vp, 0, S, tid);
-  stK.template store<C::RS>(sK[0], tid);
-  stV.template store<C::RS>(sV[0], tid);
-  if (ntiles > 1) {
-    stK.load(kp, C::BN, S - C::BN, tid);
-    stV.load(vp, C::BN, S - C::BN, tid);
-  }
+  wait_global_loads();  // the query operand above is in registers
+  Stager<T, HD, C::BN, C::NW> stK, stV;
+  stK.issue(kp, 0, S, sK[0], wave, lane, tid);
+  stV.issue(vp, 0, S, sV[0], wave, lane, tid);
+  wait_global_loads();
+  stK.commit(sK[0], tid);
+  stV.commit(sV[0], tid);
   __syncthreads();
 
   for (int j = 0; j < ntiles; ++j) {
     const int cur = j & 1;
     const int kv_t0 = j * C::BN;
-    if (j + 1 < ntiles) {  // the other buffer was last read before the previous barrier
-      stK.template store<C::RS>(sK[cur ^ 1], tid);
-      stV.template store<C::RS>(sV[cur ^ 1], tid);
-      if (j + 2 < ntiles) {
-        stK.load(kp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
-        stV.load(vp, kv_t0 + 2 * C::BN, S - kv_t0 - 2 * C::BN, tid);
-      }
+    const bool more = j + 1 < ntiles;
+    if (more) {  // the other buffer was last read before the previous barrier
+      stK.issue(kp, kv_t0 + C::BN, S, sK[cur ^ 1], wave, lane, tid);
+      stV.issue(vp, kv_t0 + C::BN, S, sV[cur ^ 1], wave, lane, tid);
     }
     if (wave_live && kv_t0 < wave_kv_end) {
       const T* tK = sK[cur];
@@ -116,9 +110,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
         act[cb] = kb0 < wave_kv_end;
         s[cb] = zero_acc();
         if (act[cb]) {
-          const T* krow = tK + (32 * cb + li) * C::RS;
 #pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks) M::mma(s[cb], row_frag_lds<T, HD>(krow, g, ks), qf[ks]);
+          for (int ks = 0; ks < C::NKS; ++ks)
+            M::mma(s[cb], row_frag_lds<T, HD, C::BN>(tK, 32 * cb + li, g, ks), qf[ks]);
           if (kb0 + 31 > q0 || kb0 + 32 > S) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -164,15 +158,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
           const typename M::frag pf = acc_frag<T>(s[cb], ks * M::KPL);
 #pragma unroll
           for (int db = 0; db < C::ND; ++db) {
-            typename M::frag a;
-            if constexpr (sizeof(T) == 2)
-              a = accrow_frag_bf16<HD, C::RS>(tV, 32 * cb + 16 * ks, 32 * db, lane);
-            else
-              a = accrow_frag_f32<C::RS>(tV + 32 * cb * C::RS, min(32 * db + li, HD - 1), g, ks);
-            M::mma(oacc[db], a, pf);
+            M::mma(oacc[db], accrow_frag<T, HD, C::BN>(tV, 32 * cb, ks, 32 * db, lane), pf);
           }
         }
       }
+    }
+    if (more) {
+      wait_global_loads();
+      stK.commit(sK[cur ^ 1], tid);
+      stV.commit(sV[cur ^ 1], tid);
     }
     __syncthreads();
   }

@@ -92,8 +92,9 @@ int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
               void* stream);
 
 /*
- * Bytes of device workspace xattn_bwd needs: 4*B*H*S (the per-row D values),
- * O(B*H*S), never S x S.  Returns 0 for invalid shapes.
+ * Bytes of device workspace xattn_bwd needs: 8*B*H*S (two floats per query
+ * row: D = rowsum(dO * o) and LSE * log2(e)), O(B*H*S), never S x S.
+ * Returns 0 for invalid shapes.
  */
 size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype);
 
@@ -120,11 +121,11 @@ int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
  * xattn_bwd(...) is exactly xattn_bwd_dq(...) followed on the same stream by
  * xattn_bwd_dkdv(...) with the same arguments and workspace.
  *
- * xattn_bwd_dq: writes dq [B][H][S][hd] float and stores D = rowsum(dO * o)
- *   ([B][H][S] float) in the workspace.
- * xattn_bwd_dkdv: writes dk, dv [B][Hkv][S][hd] float; reads D from the
- *   workspace, so it must be ordered after an xattn_bwd_dq call with the same
- *   q, o, dO, lse, shapes and workspace.
+ * xattn_bwd_dq: writes dq [B][H][S][hd] float and stores, per query row,
+ *   D = rowsum(dO * o) and LSE * log2(e) in the workspace ([2][B][H][S] float).
+ * xattn_bwd_dkdv: writes dk, dv [B][Hkv][S][hd] float; reads both per-row
+ *   values from the workspace (not lse), so it must be ordered after an
+ *   xattn_bwd_dq call with the same q, o, dO, lse, shapes and workspace.
  * Argument meaning, layout, validation and status codes are those of xattn_bwd.
  */
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,

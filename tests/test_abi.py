@@ -51,7 +51,7 @@ def bwd(L, ws=P, ws_bytes=None, B=1, S=16, H=2, Hkv=2, hd=16, scale=0.25, dtype=
     p = {n: P for n in ("q", "k", "v", "o", "lse", "dO", "dq", "dk", "dv")}
     p.update(ptrs)
     if ws_bytes is None:
-        ws_bytes = 4 * B * H * S
+        ws_bytes = 8 * B * H * S
     return L.xattn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"], p["dk"], p["dv"],
                        B, S, H, Hkv, hd, scale, dtype, ws, ws_bytes, None)
 
@@ -97,12 +97,12 @@ def test_bad_scale(L, scale):
 
 
 def test_workspace_size_and_checks(L):
-    assert L.xattn_bwd_workspace_bytes(4, 2048, 16, 16, 64, 1) == 4 * 4 * 16 * 2048
-    assert L.xattn_bwd_workspace_bytes(16, 1024, 8, 2, 64, 0) == 4 * 16 * 8 * 1024
+    assert L.xattn_bwd_workspace_bytes(4, 2048, 16, 16, 64, 1) == 8 * 4 * 16 * 2048
+    assert L.xattn_bwd_workspace_bytes(16, 1024, 8, 2, 64, 0) == 8 * 16 * 8 * 1024
     assert L.xattn_bwd_workspace_bytes(1, 16, 3, 2, 16, 0) == 0  # invalid GQA shape
     assert L.xattn_bwd_workspace_bytes(1, 16, 2, 2, 16, 9) == 0  # invalid dtype
     assert bwd(L, ws=None) == WORKSPACE
-    assert bwd(L, ws_bytes=4 * 2 * 16 - 1) == WORKSPACE
+    assert bwd(L, ws_bytes=8 * 2 * 16 - 1) == WORKSPACE
 
 
 def test_size_limits(L):

@@ -157,7 +157,7 @@ def test_outputs_fully_overwritten():
     o2 = fill(torch.empty_like(o1))
     l2 = fill(torch.empty_like(l1))
     api.fwd(t["q"], t["k"], t["v"], o=o2, lse=l2)
-    ws = fill(torch.empty(1 * 2 * 130, dtype=torch.float32, device="cuda"))
+    ws = fill(torch.empty(2 * 1 * 2 * 130, dtype=torch.float32, device="cuda"))
     g2 = [fill(torch.empty_like(x)) for x in g1]
     api.bwd(t["q"], t["k"], t["v"], o1, l1, t["dO"], dq=g2[0], dk=g2[1], dv=g2[2], workspace=ws)
     torch.cuda.synchronize()
