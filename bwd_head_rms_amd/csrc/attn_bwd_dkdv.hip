@@ -70,12 +70,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     vf[ks] = kv_ok ? row_frag_global<T, HD>(v + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
   }
 
+  // dK^T / dV^T accumulators live for the whole kernel: bf16 keeps them in AGPRs
   f32x16 dkacc[C::ND], dvacc[C::ND];
 #pragma unroll
   for (int d = 0; d < C::ND; ++d) {
     dkacc[d] = zero_acc();
     dvacc[d] = zero_acc();
   }
+  auto acc_mma = [](f32x16& acc, const typename M::frag& a, const typename M::frag& b) {
+    if constexpr (sizeof(T) == 2)
+      mma_agpr(acc, a, b);
+    else
+      M::mma(acc, a, b);
+  };
 
   const int qt_first = (kt * C::BN) / C::BMQ;
   const int nq = (S + C::BMQ - 1) / C::BMQ;
@@ -92,14 +99,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const int row0 = qt * C::BMQ;
     stQ.issue(q + bh * S * HD, row0, S, sQ[buf], wave, lane, tid);
     stO.issue(dO + bh * S * HD, row0, S, sO[buf], wave, lane, tid);
-    // per-row statistics: 64 rows per wave instruction, rows past S read row S-1
+    // per-row statistics: 64 rows per wave instruction, rows past S read zero
     constexpr int NST = C::BMQ / kWave;
+    const v4i rl = make_rsrc(lse2 + bh * S, (uint32_t)S * 4u);
+    const v4i rd = make_rsrc(dws + bh * S, (uint32_t)S * 4u);
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       if (wave == i) {
-        const int qi = min(row0 + kWave * i + lane, S - 1);
-        lds_copy4(lse2 + bh * S + qi, &sL[buf][kWave * i]);
-        lds_copy4(dws + bh * S + qi, &sD[buf][kWave * i]);
+        const uint32_t voff = (uint32_t)(kWave * i + lane) * 4u;
+        lds_copy4(rl, voff, (uint32_t)row0 * 4u, &sL[buf][kWave * i]);
+        lds_copy4(rd, voff, (uint32_t)row0 * 4u, &sD[buf][kWave * i]);
       }
     }
   };
@@ -151,17 +160,86 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           const typename M::frag sf = acc_frag<T>(dp, ks * M::KPL);
 #pragma unroll
           for (int db = 0; db < C::ND; ++db) {
-            M::mma(dvacc[db], accrow_frag<T, HD, C::BMQ>(tO, 32 * qb, ks, 32 * db, lane), pf);
-            M::mma(dkacc[db], accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane), sf);
+            acc_mma(dvacc[db], accrow_frag<T, HD, C::BMQ>(tO, 32 * qb, ks, 32 * db, lane), pf);
+            acc_mma(dkacc[db], accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane), sf);
           }
         }
       };
 
       const int qt0 = qt * C::BMQ;
       if (qt0 >= kv0 + 32 && qt0 + C::BMQ <= S) {
-        // every block of the tile is below the diagonal and inside the sequence
+        // Every block of the tile is below the diagonal and inside the
+        // sequence.  Phases are pinned with scheduling barriers so that each
+        // LDS operand is read a whole phase before the instruction that needs
+        // it (the loads would otherwise sit right in front of their MFMAs):
+        //   [S, dP MFMAs of block qb] [transpose operands and row statistics
+        //   of qb] [softmax-gradient VALU of qb] [dV, dK MFMAs of qb; row
+        //   operands of qb+1]
+        if constexpr (sizeof(T) == 2) {
+          typename M::frag aq[C::NKS], ao[C::NKS];
 #pragma unroll
-        for (int qb = 0; qb < C::NQB; ++qb) block(qb, std::false_type{});
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            aq[ks] = row_frag_lds<T, HD, C::BMQ>(tQ, li, g, ks);
+            ao[ks] = row_frag_lds<T, HD, C::BMQ>(tO, li, g, ks);
+          }
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) {
+            f32x16 s = zero_acc(), dp = zero_acc();
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) {
+              M::mma(s, aq[ks], kf[ks]);
+              M::mma(dp, ao[ks], vf[ks]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            typename M::frag to[C::NAS][C::ND], tq[C::NAS][C::ND];
+#pragma unroll
+            for (int ks = 0; ks < C::NAS; ++ks)
+#pragma unroll
+              for (int db = 0; db < C::ND; ++db) {
+                to[ks][db] = accrow_frag<T, HD, C::BMQ>(tO, 32 * qb, ks, 32 * db, lane);
+                tq[ks][db] = accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane);
+              }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const float4 lv = *reinterpret_cast<const float4*>(tL + 32 * qb + 8 * rg + 4 * g);
+              const float4 dv4 = *reinterpret_cast<const float4*>(tD + 32 * qb + 8 * rg + 4 * g);
+              const float lr[4] = {lv.x, lv.y, lv.z, lv.w}, dr[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * rg + e;
+                const float p = fast_exp2(fmaf(s[r], c, -lr[e]));
+                s[r] = p;
+                dp[r] = p * (dp[r] - dr[e]);  // dS
+              }
+            }
+            typename M::frag pf[C::NAS], sf[C::NAS];
+#pragma unroll
+            for (int ks = 0; ks < C::NAS; ++ks) {
+              pf[ks] = acc_frag<T>(s, ks * M::KPL);
+              sf[ks] = acc_frag<T>(dp, ks * M::KPL);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < C::NAS; ++ks)
+#pragma unroll
+              for (int db = 0; db < C::ND; ++db) {
+                acc_mma(dvacc[db], to[ks][db], pf[ks]);
+                acc_mma(dkacc[db], tq[ks][db], sf[ks]);
+              }
+            if (qb + 1 < C::NQB) {
+#pragma unroll
+              for (int ks = 0; ks < C::NKS; ++ks) {
+                aq[ks] = row_frag_lds<T, HD, C::BMQ>(tQ, 32 * (qb + 1) + li, g, ks);
+                ao[ks] = row_frag_lds<T, HD, C::BMQ>(tO, 32 * (qb + 1) + li, g, ks);
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < C::NQB; ++qb) block(qb, std::false_type{});
+        }
       } else {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
@@ -178,6 +256,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     __syncthreads();
   }
 
+  if constexpr (sizeof(T) == 2) mma_agpr_drain();
   if (!wave_live || !kv_ok) return;
   float* krow = dk + kvplane + (size_t)my_kv * HD;
   float* vrow = dv + kvplane + (size_t)my_kv * HD;

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       df[ks] = zero_frag<T>();
     }
   }
-  const float Drow = Dp + __shfl_xor(Dp, 32);
+  const float Drow = halves_sum(Dp);
   const float lse2 = q_ok ? lse[(size_t)bh * S + my_q] * kLog2e : 0.f;
   if (q_ok && g == 0) {
     dws[(size_t)bh * S + my_q] = Drow;

@@ -38,6 +38,19 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Combine lanes l and l^32 (v_permlane32_swap exchanges the two half-waves: the
+// two results hold x of lanes 0..31 and 32..63 in every lane's position).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                                  __builtin_bit_cast(int, x), false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 template <typename T> struct Mma;
@@ -62,6 +75,17 @@ template <> struct Mma<bf16> {
   }
 };
 
+// Accumulation into an accumulator kept in AGPRs (bf16 operands).  Written as
+// inline assembly so that long-lived accumulators stay in the AGPR file and the
+// VGPR file is left to the tiles that VALU code post-processes.  The compiler
+// cannot see hazards inside the assembly, so it carries its own wait states: two
+// before the MFMA (a VALU write of an operand just before), and mma_agpr_drain()
+// (24) must run between the last accumulation and any read of the result.
+__device__ __forceinline__ void mma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_agpr_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"); }
+
 // ---------------------------------------------------------------------------
 // fp32 -> operand conversion of accumulator registers [r0, r0 + KPL)
 template <typename T>
@@ -69,6 +93,19 @@ __device__ __forceinline__ typename Mma<T>::frag acc_frag(const f32x16& x, int r
 
 template <>
 __device__ __forceinline__ float acc_frag<float>(const f32x16& x, int r0) { return x[r0]; }
+
+// Sum of the eight bf16 values of an operand fragment, added to `acc`
+// (v_dot2_f32_bf16 against (1, 1): four instructions, fp32 accumulation).
+__device__ __forceinline__ float frag_sum(const bf16x8& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(float f, float acc) { return acc + f; }
 
 template <>
 __device__ __forceinline__ bf16x8 acc_frag<bf16>(const f32x16& x, int r0) {
@@ -95,36 +132,46 @@ __device__ __forceinline__ typename Mma<T>::frag row_frag_global(const T* row, i
 // LDS tiles of ROWS x HD elements.
 //
 // bf16: rows of HD elements with no padding, filled by global_load_lds_dwordx4
-//   (each lane's 16 bytes land at the instruction's LDS base + 16 * lane, so a
-//   wave instruction writes 1 KB of consecutive rows and no per-row padding is
-//   possible).  Instead the 16-byte chunks of each row are XOR-swizzled by row:
+//   (buffer_load_dwordx4 with lds: each lane's 16 bytes land at the
+//   instruction's LDS base + 16 * lane, so a wave instruction writes 1 KB of
+//   consecutive rows and no per-row padding is possible).  Instead the 16-byte chunks of each row are XOR-swizzled by row:
 //   logical chunk c of row r lives at physical chunk c ^ swz(r).  swz is chosen
 //   (for 64 banks of 4 bytes) so that both read patterns are conflict free: 16
 //   lanes reading one chunk of 16 consecutive rows, and the transpose reads
 //   (4 consecutive rows x 4 consecutive chunks per half wave).  Rows past the
-//   sequence end are loaded from row S-1 (finite data; the mask removes them).
+//   sequence end read as zero.
 // fp32: rows padded to HD+1 elements (odd stride), staged through registers.
-// One wave instruction copying 16 bytes per lane from global memory into LDS:
-// lane l's bytes land at lds_dst + 16*l (global_load_lds_dwordx4, base in M0).
-// Written as inline assembly so that the compiler does not treat the copy in
-// flight into one buffer as a hazard for reads of the other buffer (it would
-// otherwise wait for the copy before every LDS read); completion is awaited
-// explicitly (wait_global_loads) before the barrier that publishes the tile.
-__device__ __forceinline__ void lds_copy16(const void* src, const void* lds_dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(base)
-               : "memory", "m0");
+// Raw buffer resource (gfx9 layout) for `bytes` bytes at `base`: loads at byte
+// offsets past the end return zero.  All fields are wave-uniform.
+typedef int v4i __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+             __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu)),
+             __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
-// Same with 4 bytes per lane (global_load_lds_dword): lane l's dword lands at
-// lds_dst + 4*l.
-__device__ __forceinline__ void lds_copy4(const void* src, const void* lds_dst) {
+// One wave instruction copying 16 (or 4) bytes per lane from a buffer into LDS:
+// lane l's bytes, read at byte offset voff + soff, land at lds_dst + 16*l (4*l)
+// (buffer_load_dwordx4 / _dword with lds, LDS base in M0).  Written as inline
+// assembly so that the compiler does not treat a copy in flight into one buffer
+// as a hazard for reads of the other buffer (it would otherwise wait for the
+// copy before every LDS read); completion is awaited explicitly
+// (wait_global_loads) before the barrier that publishes the tile.
+__device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff, uint32_t soff,
+                                           const void* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "v"(src), "s"(base)
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(v4i rsrc, uint32_t voff, uint32_t soff,
+                                          const void* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(base)
                : "memory", "m0");
 }
 
@@ -148,17 +195,19 @@ struct Tile<bf16, HD, ROWS> {
   __device__ static int off(int r, int col) {
     return r * HD + ((((col >> 3) ^ swz(r))) << 3) + (col & 7);
   }
-  // Issue the asynchronous copy of rows [row0, row0 + ROWS) of a head plane
-  // (row stride HD) into `tile`, shared by NW waves.  Completion is tracked by
-  // vmcnt: wait for it before the barrier that publishes the tile.
+  // Issue the asynchronous copy of rows [row0, row0 + ROWS) of a head plane of
+  // S rows (row stride HD) into `tile`, shared by NW waves; rows past S read
+  // zero.  Completion is tracked by vmcnt: wait for it before the barrier that
+  // publishes the tile.
   template <int NW>
   __device__ static void issue(const bf16* plane, int row0, int S, bf16* tile, int wave, int lane) {
+    const v4i rsrc = make_rsrc(plane, (uint32_t)S * HD * 2u);
+    const uint32_t soff = (uint32_t)row0 * HD * 2u;
 #pragma unroll
     for (int i = wave; i < NINST; i += NW) {
       const int r = i * ROWS_PER_INST + lane / CPR;
       const int chunk = (lane % CPR) ^ swz(r);
-      const int gr = min(row0 + r, S - 1);
-      lds_copy16(plane + (size_t)gr * HD + chunk * 8, tile + i * 512);
+      lds_copy16(rsrc, (uint32_t)(r * HD + chunk * 8) * 2u, soff, tile + i * 512);
     }
   }
 };

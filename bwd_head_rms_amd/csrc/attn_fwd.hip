@@ -8,10 +8,11 @@
 //   S^T = K . Q^T            (MFMA; keys are rows, queries are lanes, so every
 //                              softmax row lives in one lane pair)
 //   online softmax in the log2 domain: reference max m and sum l per query,
-//   P = exp2(S*scale*log2e - m), rescale of the output accumulator by
-//   exp2(m_old - m_new) when a row's max grows past its slack (the online
-//   softmax of the fused kernel in the "xtrain evolution overview", infra
-//   table row T14)
+//   P = exp2(S*scale*log2e - m) (the row sum l accumulates P as rounded for
+//   the product below); the row max is only taken, and the accumulator
+//   rescaled by exp2(m_old - m_new), when the weights of a row outgrow a wide
+//   bound (the online softmax of the fused kernel in the "xtrain evolution
+//   overview", infra table row T14)
 //   O^T += V^T . P^T          (MFMA; P feeds the product from registers, V^T
 //                              comes from the row-major tile by transpose reads)
 // Tiles wholly above the diagonal are never visited; blocks of 32 keys wholly
@@ -25,10 +26,10 @@
 
 namespace xattn {
 
-// Slack (log2 units) a row's scores may exceed its reference max before the
-// output accumulator is rescaled: probabilities stay below 2^8 = 256, far
-// from fp32 or bf16 overflow, and the sum l below 256 * S.
-constexpr float kRescaleSlack = 8.f;
+// Bound on a row's per-tile sum of weights exp2(S*c - m) before its reference
+// max m is renewed: weights stay below 2^64 (bf16 and fp32 reach 2^127), and the
+// row sum l below 2^64 * S, so no precision or range is lost.
+constexpr float kRescaleBound = 18446744073709551616.f;  // 2^64
 
 template <typename T, int HD>
 struct FwdCfg {
@@ -102,65 +103,84 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
       // 32-aligned like the wave's rows: a visited block is wholly visible or
       // the diagonal block, and only the diagonal block and the sequence tail
       // carry a mask (masked scores become -inf, i.e. weight exactly 0).
-      f32x16 s[C::NB];
       bool act[C::NB];
 #pragma unroll
-      for (int cb = 0; cb < C::NB; ++cb) {
-        const int kb0 = kv_t0 + 32 * cb;
-        act[cb] = kb0 < wave_kv_end;
-        s[cb] = zero_acc();
-        if (act[cb]) {
+      for (int cb = 0; cb < C::NB; ++cb) act[cb] = kv_t0 + 32 * cb < wave_kv_end;
+      f32x16 s[C::NB];
+      auto scores = [&]() {
 #pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks)
-            M::mma(s[cb], row_frag_lds<T, HD, C::BN>(tK, 32 * cb + li, g, ks), qf[ks]);
-          if (kb0 + 31 > q0 || kb0 + 32 > S) {
+        for (int cb = 0; cb < C::NB; ++cb) {
+          const int kb0 = kv_t0 + 32 * cb;
+          s[cb] = zero_acc();
+          if (act[cb]) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kv = kb0 + acc_row(r, g);
-              s[cb][r] = (kv <= my_q && kv < S) ? s[cb][r] : -INFINITY;
+            for (int ks = 0; ks < C::NKS; ++ks)
+              M::mma(s[cb], row_frag_lds<T, HD, C::BN>(tK, 32 * cb + li, g, ks), qf[ks]);
+            if (kb0 + 31 > q0 || kb0 + 32 > S) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int kv = kb0 + acc_row(r, g);
+                s[cb][r] = (kv <= my_q && kv < S) ? s[cb][r] : -INFINITY;
+              }
             }
           }
         }
-      }
-      float mx = -INFINITY;
+      };
+      // P = exp2(S*c - m) as operand fragments, and the row's partial sum of P
+      // (the same rounded weights that enter the product below).
+      typename M::frag pf[C::NB][C::NAS];
+      float tsum = 0.f;
+      auto probs = [&]() {
+        tsum = 0.f;
 #pragma unroll
-      for (int cb = 0; cb < C::NB; ++cb)
-        if (act[cb]) {
+        for (int cb = 0; cb < C::NB; ++cb) {
+          if (!act[cb]) continue;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
+          for (int r = 0; r < 16; ++r) s[cb][r] = fast_exp2(fmaf(s[cb][r], c, -m));
+#pragma unroll
+          for (int ks = 0; ks < C::NAS; ++ks) {
+            pf[cb][ks] = acc_frag<T>(s[cb], ks * M::KPL);
+            tsum = frag_sum(pf[cb][ks], tsum);
+          }
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-      // Lazy rescale: a row keeps its reference max m while its scores stay
-      // below m + kRescaleSlack (log2 units), so P <= 2^kRescaleSlack and the
-      // accumulator is rescaled only when some row's max really grows.  The
-      // decision is per row (rows that do not need it multiply by exactly 1),
-      // so every row's result depends only on that row's scores.
-      const bool grow = mx > m + kRescaleSlack;
-      if (__ballot(grow)) {
-        const float m_new = grow ? mx : m;
-        const float alpha = grow ? fast_exp2(m - m_new) : 1.f;
+      };
+      scores();
+      probs();
+      // Each row keeps a reference max m and uses it as long as its weights
+      // stay below 2^kRescaleSlack (their sum bounds every weight).  Only when
+      // that fails -- the row's first tile (m = -inf), or scores that really
+      // outgrew m -- are the scores recomputed, the row max taken and the
+      // accumulator rescaled.  The decision is per row (rows that pass keep m
+      // and recompute the same weights), so every row's result depends only
+      // on that row's scores.
+      const bool fail = halves_max(tsum <= kRescaleBound ? 0.f : 1.f) != 0.f;
+      if (__ballot(fail)) {
+        scores();
+        float mx = -INFINITY;
+#pragma unroll
+        for (int cb = 0; cb < C::NB; ++cb)
+          if (act[cb]) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
+          }
+        mx = halves_max(mx) * c;
+        const float m_new = fail ? fmaxf(m, mx) : m;
+        const float alpha = fail ? fast_exp2(m - m_new) : 1.f;
         m = m_new;
         l *= alpha;
 #pragma unroll
         for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
+        probs();
       }
+      l += tsum;
 #pragma unroll
       for (int cb = 0; cb < C::NB; ++cb) {
         if (!act[cb]) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[cb][r], c, -m));
-          s[cb][r] = p;
-          l += p;
-        }
+        for (int ks = 0; ks < C::NAS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < C::NAS; ++ks) {
-          const typename M::frag pf = acc_frag<T>(s[cb], ks * M::KPL);
-#pragma unroll
-          for (int db = 0; db < C::ND; ++db) {
-            M::mma(oacc[db], accrow_frag<T, HD, C::BN>(tV, 32 * cb, ks, 32 * db, lane), pf);
-          }
-        }
+          for (int db = 0; db < C::ND; ++db)
+            M::mma(oacc[db], accrow_frag<T, HD, C::BN>(tV, 32 * cb, ks, 32 * db, lane), pf[cb][ks]);
       }
     }
     if (more) {
@@ -172,7 +192,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   }
 
   if (!wave_live) return;
-  l += __shfl_xor(l, 32);
+  l = halves_sum(l);
   const float inv = 1.f / l;
   if (q_ok) {
     T* orow = o + ((size_t)bh * S + my_q) * HD;
