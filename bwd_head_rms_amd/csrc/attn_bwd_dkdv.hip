@@ -106,9 +106,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       if (wave == i) {
-        const uint32_t voff = (uint32_t)(kWave * i + lane) * 4u;
-        lds_copy4(rl, voff, (uint32_t)row0 * 4u, &sL[buf][kWave * i]);
-        lds_copy4(rd, voff, (uint32_t)row0 * 4u, &sD[buf][kWave * i]);
+        const uint32_t voff = (uint32_t)(row0 + kWave * i + lane) * 4u;
+        lds_copy4(rl, voff, &sL[buf][kWave * i]);
+        lds_copy4(rd, voff, &sD[buf][kWave * i]);
       }
     }
   };

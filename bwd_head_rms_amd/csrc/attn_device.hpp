@@ -152,26 +152,27 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // One wave instruction copying 16 (or 4) bytes per lane from a buffer into LDS:
-// lane l's bytes, read at byte offset voff + soff, land at lds_dst + 16*l (4*l)
-// (buffer_load_dwordx4 / _dword with lds, LDS base in M0).  Written as inline
+// lane l's bytes, read at byte offset voff, land at lds_dst + 16*l (4*l)
+// (buffer_load_dwordx4 / _dword with lds, LDS base in M0).  The whole offset
+// is passed in the VGPR operand, the part of the address that the buffer range
+// check covers (the SGPR offset is added after the check), so every byte at or
+// past the end of the resource reads as zero.  Written as inline
 // assembly so that the compiler does not treat a copy in flight into one buffer
 // as a hazard for reads of the other buffer (it would otherwise wait for the
 // copy before every LDS read); completion is awaited explicitly
 // (wait_global_loads) before the barrier that publishes the tile.
-__device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff, uint32_t soff,
-                                           const void* lds_dst) {
+__device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff, const void* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(soff), "s"(base)
+               : "v"(voff), "s"(rsrc), "s"(base)
                : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copy4(v4i rsrc, uint32_t voff, uint32_t soff,
-                                          const void* lds_dst) {
+__device__ __forceinline__ void lds_copy4(v4i rsrc, uint32_t voff, const void* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(soff), "s"(base)
+               : "v"(voff), "s"(rsrc), "s"(base)
                : "memory", "m0");
 }
 
@@ -202,12 +203,11 @@ struct Tile<bf16, HD, ROWS> {
   template <int NW>
   __device__ static void issue(const bf16* plane, int row0, int S, bf16* tile, int wave, int lane) {
     const v4i rsrc = make_rsrc(plane, (uint32_t)S * HD * 2u);
-    const uint32_t soff = (uint32_t)row0 * HD * 2u;
 #pragma unroll
     for (int i = wave; i < NINST; i += NW) {
       const int r = i * ROWS_PER_INST + lane / CPR;
       const int chunk = (lane % CPR) ^ swz(r);
-      lds_copy16(rsrc, (uint32_t)(r * HD + chunk * 8) * 2u, soff, tile + i * 512);
+      lds_copy16(rsrc, (uint32_t)((row0 + r) * HD + chunk * 8) * 2u, tile + i * 512);
     }
   }
 };

@@ -164,3 +164,30 @@ def test_outputs_fully_overwritten():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,S,hd", [("bf16", 130, 64), ("bf16", 100, 32), ("bf16", 77, 16),
+                                        ("f32", 130, 64)])
+def test_no_reads_past_input_ends(dtype, S, hd):
+    """Every input tensor is followed in memory by NaN: the kernels must never
+    read past the end of a (batch, head) plane (the tail tile of a ragged
+    sequence included), so the results equal those of ordinary allocations."""
+    import torch
+    from bwd_head_rms_amd import api
+    arrs = _gen(1, S, 4, 2, hd, dtype)
+    t = H.to_dev(arrs, dtype)
+
+    def guarded(x):
+        buf = torch.full((x.numel() + 8192,), float("nan"), dtype=x.dtype, device=x.device)
+        buf[: x.numel()].copy_(x.reshape(-1))
+        return buf[: x.numel()].view(x.shape)
+
+    g = {n: guarded(x) for n, x in t.items()}
+    o1, l1 = api.fwd(t["q"], t["k"], t["v"])
+    r1 = api.bwd(t["q"], t["k"], t["v"], o1, l1, t["dO"])
+    o2, l2 = api.fwd(g["q"], g["k"], g["v"])
+    r2 = api.bwd(g["q"], g["k"], g["v"], guarded(o1), guarded(l1), g["dO"])
+    torch.cuda.synchronize()
+    for a, b in zip((o1, l1, *r1), (o2, l2, *r2)):
+        assert torch.isfinite(b.float()).all()
+        assert torch.equal(a, b)
