@@ -21,6 +21,8 @@
 // natural-log LSE = (m + log2 l) * ln 2.  Query head h reads kv head
 // h / (H / Hkv) by address (GQA without a copy, row T15 of the same table).
 // Work order: heaviest query tiles first.
+#include <type_traits>
+
 #include "attn_device.hpp"
 #include "launch.hpp"
 
@@ -209,6 +211,292 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16: software-pipelined forward.  Same work split (4 waves x 32 query rows
+// per workgroup), but each wave walks its key range in 32-key blocks and, in
+// sub-step i, overlaps three stages of consecutive blocks:
+//   A(i+1): S^T_{i+1} = K_{i+1} . Q^T            (matrix cores)
+//   B(i)  : P_i = exp2(S_i*c - m), row sums      (vector ALU)
+//   C(i-1): O^T += V_{i-1}^T . P_{i-1}^T         (matrix cores)
+// so the matrix cores work while the softmax of the previous block runs,
+// instead of one wave stalling on the chain S -> softmax -> P.V of a single
+// block.  K and V blocks are copied straight from HBM into rings of four
+// 32-row LDS slots; one step (one barrier) covers two sub-steps, i.e. 64 keys,
+// and copies the four blocks the next step reads.  The loop is unrolled over
+// the ring so every slot address is a constant.
+//
+// Softmax reference: step 0 (the first block) uses the exact online update
+// (m starts at -inf).  Later sub-steps keep m and only check that each row's
+// weights exp2(S*c - m) stay below 2^63 per half block (no overflow or loss of
+// precision in bf16/fp32).  A row that ever fails that check is recomputed at
+// the end by an exact, unpipelined pass over HBM (scores that rise by more
+// than ~44 natural-log units past the first block's max; never seen with
+// normalised inputs).  Every row's result depends only on its own scores.
+template <int HD>
+struct FwdPipe {
+  static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW;
+  static constexpr int NKS = HD / 16;                // S contraction steps
+  static constexpr int ND = HD >= 32 ? HD / 32 : 1;  // output column blocks
+  static constexpr int NAS = 2;                      // key steps per block
+  static constexpr int NC = NAS * ND;                // P.V products per block
+  static constexpr int NSL = 4;                      // ring slots (K and V)
+  using TL = Tile<bf16, HD, 32>;
+  static constexpr int TE = TL::ELEMS;
+  static constexpr int CPR = TL::CPR, RPI = TL::ROWS_PER_INST, NINST = TL::NINST;
+  static_assert(NINST <= NW, "one copy per wave and block");
+};
+
+constexpr float kHalfBlockBound = 9223372036854775808.f;  // 2^63
+
+template <int HD>
+__global__ __launch_bounds__(256) void attn_fwd_pipe_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    bf16* __restrict__ o, float* __restrict__ lse, int S, int H, int Hkv, int nqt, int BH,
+    float c) {
+  using P = FwdPipe<HD>;
+  using M = Mma<bf16>;
+  using frag = M::frag;
+  __shared__ __align__(16) bf16 sK[P::NSL][P::TE];
+  __shared__ __align__(16) bf16 sV[P::NSL][P::TE];
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int li = lane & 31, g = lane >> 5;
+  const int bid = blockIdx.x;
+  const int qt = nqt - 1 - bid / BH;
+  const int bh = bid % BH;
+  const int b = bh / H, h = bh % H;
+  const int kvh = h / (H / Hkv);
+  const bf16* qp = q + (size_t)bh * S * HD;
+  const size_t kvoff = ((size_t)b * Hkv + kvh) * S * HD;
+
+  const int q0 = qt * P::BM + wave * 32;
+  const int my_q = q0 + li;
+  const bool q_ok = my_q < S;
+  // Blocks of the workgroup and of this wave; a wave's last block is its
+  // diagonal block, which also holds the end of the sequence when S is ragged.
+  // A wave wholly past the end (last tile of a ragged sequence) runs over all
+  // blocks like a live one and stores nothing.
+  const int nbw = (min(S, qt * P::BM + P::BM) + 31) / 32;
+  const int nb = (min(S, q0 + 32) + 31) / 32;
+
+  f32x16 oacc[P::ND];
+#pragma unroll
+  for (int d = 0; d < P::ND; ++d) oacc[d] = zero_acc();
+  float m = -INFINITY, l = 0.f;
+  bool bad = false;  // this lane's half of the row failed the weight bound
+
+  // Copies: wave w < NINST copies rows w*RPI .. +RPI-1 of a block; a block past
+  // the workgroup's last one is addressed past the end of the plane and reads
+  // zero without a memory access.
+  const uint32_t plane_bytes = (uint32_t)S * HD * 2u;
+  const v4i rK = make_rsrc(k + kvoff, plane_bytes);
+  const v4i rV = make_rsrc(v + kvoff, plane_bytes);
+  const int crow = wave * P::RPI + lane / P::CPR;
+  const uint32_t cvoff = (uint32_t)(crow * HD + (((lane % P::CPR) ^ P::TL::swz(crow)) << 3)) * 2u;
+  auto copy = [&](const v4i& rs, bf16* slot, int blk) __attribute__((always_inline)) {
+    if (wave < P::NINST)
+      lds_copy16(rs, cvoff + (blk < nbw ? (uint32_t)blk * 32u * HD * 2u : plane_bytes),
+                 slot + wave * 512);
+  };
+
+  // first copies (K_0..K_3, V_0, V_1) and the query operand, in flight together
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) copy(rK, sK[blk], blk);
+  copy(rV, sV[0], 0);
+  copy(rV, sV[1], 1);
+  frag qf[P::NKS];
+#pragma unroll
+  for (int ks = 0; ks < P::NKS; ++ks)
+    qf[ks] = q_ok ? row_frag_global<bf16, HD>(qp + (size_t)my_q * HD, g, ks) : zero_frag<bf16>();
+  wait_global_loads();
+  __syncthreads();
+
+  // S^T of the block in K slot `slot`
+  auto scores = [&](int slot, f32x16& s) __attribute__((always_inline)) {
+    const bf16* tK = sK[slot];
+    s = zero_acc();
+#pragma unroll
+    for (int ks = 0; ks < P::NKS; ++ks) M::mma(s, row_frag_lds<bf16, HD, 32>(tK, li, g, ks), qf[ks]);
+  };
+  // weights exp2(s*c - m) as operand fragments; returns their sum over this
+  // lane's half of the block (the same rounded weights that enter the product)
+  auto weights = [&](f32x16& s, frag* p) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], c, -m));
+    p[0] = acc_frag<bf16>(s, 0);
+    p[1] = acc_frag<bf16>(s, 8);
+    return frag_sum(p[0], 0.f) + frag_sum(p[1], 0.f);
+  };
+  // diagonal block / sequence end: scores of keys past a row or past S are -inf
+  auto mask = [&](int i, f32x16& s) __attribute__((always_inline)) {
+    const int kb0 = 32 * i;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kv = kb0 + acc_row(r, g);
+      s[r] = (kv <= my_q && kv < S) ? s[r] : -INFINITY;
+    }
+  };
+
+  // Step 0: A(0), A(1), B(0) with the exact update (m starts at -inf).
+  // Afterwards sA = S_1 and pA = P_0, the roles sub-step 1 expects.
+  f32x16 sA, sB;
+  frag pA[2], pB[2];
+  scores(0, sB);
+  scores(1, sA);
+  if (nb == 1) mask(0, sB);
+  {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sB[r]);
+    m = halves_max(mx) * c;  // finite: every row sees key 0
+    l = weights(sB, pA);
+  }
+  __syncthreads();  // K_0, K_1 read before step 1 refills their slots
+
+  // Sub-step i >= 1, J = i mod 4 (fixes the slots): A(i+1), B(i), C(i-1), the
+  // same code for every wave, software-pipelined.  From its diagonal block on
+  // (i >= nb-1) a wave masks B(i): past its rows every score is -inf, every
+  // weight 0, so its last sub-steps add nothing and its A products are unused.
+  // Only the mask is a branch, before the pipelined region; the products always
+  // run, so the accumulators never change registers.
+  auto sub = [&](auto jtag, f32x16& s_cur, f32x16& s_nxt, frag* p_prev, frag* p_cur,
+                 int i) __attribute__((always_inline)) {
+    constexpr int J = decltype(jtag)::value;
+    if (i + 1 >= nb) mask(i, s_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    // operands of both products first, so their LDS latency overlaps the
+    // softmax arithmetic
+    const bf16* tK = sK[(J + 1) % P::NSL];
+    const bf16* tV = sV[(J + P::NSL - 1) % P::NSL];
+    frag kf[P::NKS], vf[P::NC];
+#pragma unroll
+    for (int ks = 0; ks < P::NKS; ++ks) kf[ks] = row_frag_lds<bf16, HD, 32>(tK, li, g, ks);
+#pragma unroll
+    for (int t = 0; t < P::NC; ++t)
+      vf[t] = accrow_frag<bf16, HD, 32>(tV, 0, t / P::ND, 32 * (t % P::ND), lane);
+    // A(i+1) first: the next sub-step's softmax waits for its result
+    s_nxt = zero_acc();
+#pragma unroll
+    for (int t = 0; t < P::NKS; ++t) M::mma(s_nxt, kf[t], qf[t]);
+    float tsum = weights(s_cur, p_cur);
+    // keep B(i) in this sub-step (it would otherwise sink next to its use in C(i))
+    asm volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]), "+v"(tsum));
+#pragma unroll
+    for (int t = 0; t < P::NC; ++t) M::mma(oacc[t % P::ND], vf[t], p_prev[t / P::ND]);
+    bad = bad || !(tsum <= kHalfBlockBound);
+    l += tsum;
+    // issue order: LDS reads, A(i+1) (queued on the matrix cores), the
+    // softmax arithmetic, then C(i-1)
+    __builtin_amdgcn_sched_group_barrier(0x100, P::NKS + 2 * P::NC, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, P::NKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 60, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, P::NC, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Step u >= 1 (sub-steps 2u-1 and 2u; J0 = (2u-1) mod 4): first copies the
+  // blocks of step u+1 (K_{2u+2}, K_{2u+3}, V_{2u}, V_{2u+1}; their slots were
+  // last read in step u-1), then both sub-steps, then waits for the copies
+  // and the barrier that publishes them.
+  auto step = [&](auto j0tag, int u) __attribute__((always_inline)) {
+    constexpr int J0 = decltype(j0tag)::value;  // 1 or 3
+    __builtin_amdgcn_sched_barrier(0);
+    copy(rK, sK[(J0 + 3) % P::NSL], 2 * u + 2);
+    copy(rK, sK[(J0 + 4) % P::NSL], 2 * u + 3);
+    copy(rV, sV[(J0 + 1) % P::NSL], 2 * u);
+    copy(rV, sV[(J0 + 2) % P::NSL], 2 * u + 1);
+    sub(std::integral_constant<int, J0>{}, sA, sB, pA, pB, 2 * u - 1);
+    sub(std::integral_constant<int, (J0 + 1) % P::NSL>{}, sB, sA, pB, pA, 2 * u);
+    wait_global_loads();
+    __syncthreads();
+  };
+
+  // steps 1 .. ceil(nbw/2): sub-step nbw is the drain of the last wave
+  for (int u = 1;; u += 2) {
+    step(std::integral_constant<int, 1>{}, u);
+    if (2 * u >= nbw) break;
+    step(std::integral_constant<int, 3>{}, u + 1);
+    if (2 * u + 2 >= nbw) break;
+  }
+
+  if (q0 >= S) return;
+  const bool row_bad = halves_max(bad ? 1.f : 0.f) != 0.f;
+  if (__builtin_expect(__ballot(row_bad) != 0, 0)) {
+    // exact recompute of this wave's rows from HBM: running max, rescale per
+    // block; only the failed rows take its result
+    const bf16* kp = k + kvoff;
+    const bf16* vp = v + kvoff;
+    f32x16 acc2[P::ND];
+#pragma unroll
+    for (int d = 0; d < P::ND; ++d) acc2[d] = zero_acc();
+    float m2 = -INFINITY, l2 = 0.f;
+    for (int j = 0; j < nb; ++j) {
+      const int key = 32 * j + li;
+      f32x16 s2 = zero_acc();
+#pragma unroll
+      for (int ks = 0; ks < P::NKS; ++ks)
+        M::mma(s2, key < S ? row_frag_global<bf16, HD>(kp + (size_t)key * HD, g, ks) : zero_frag<bf16>(),
+               qf[ks]);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kv = 32 * j + acc_row(r, g);
+        s2[r] = (kv <= my_q && kv < S) ? s2[r] : -INFINITY;
+        mx = fmaxf(mx, s2[r]);
+      }
+      const float m_new = fmaxf(m2, halves_max(mx) * c);
+      const float alpha = m_new == m2 ? 1.f : fast_exp2(m2 - m_new);
+      m2 = m_new;
+      l2 *= alpha;
+#pragma unroll
+      for (int d = 0; d < P::ND; ++d) acc2[d] *= alpha;
+      frag p2[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s2[r] = fast_exp2(fmaf(s2[r], c, -m2));
+      p2[0] = acc_frag<bf16>(s2, 0);
+      p2[1] = acc_frag<bf16>(s2, 8);
+      l2 += frag_sum(p2[0], 0.f) + frag_sum(p2[1], 0.f);
+#pragma unroll
+      for (int ks = 0; ks < P::NAS; ++ks)
+#pragma unroll
+        for (int db = 0; db < P::ND; ++db) {
+          // V^T operand: head-dim column 32*db + li (clamped for hd 16), keys
+          // of the permuted contraction order, read one by one
+          const int d = min(32 * db + li, HD - 1);
+          frag vf;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int kv = 32 * j + acc_row(8 * ks + t, g);
+            vf[t] = kv < S ? vp[(size_t)kv * HD + d] : (bf16)0.f;
+          }
+          M::mma(acc2[db], vf, p2[ks]);
+        }
+    }
+    if (row_bad) {
+      m = m2;
+      l = l2;
+#pragma unroll
+      for (int d = 0; d < P::ND; ++d) oacc[d] = acc2[d];
+    }
+  }
+
+  l = halves_sum(l);
+  const float inv = 1.f / l;
+  if (q_ok) {
+    bf16* orow = o + ((size_t)bh * S + my_q) * HD;
+#pragma unroll
+    for (int db = 0; db < P::ND; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = 32 * db + 8 * rg + 4 * g;
+        if (d0 < HD)
+          store4<bf16>(orow + d0, oacc[db][4 * rg] * inv, oacc[db][4 * rg + 1] * inv,
+                       oacc[db][4 * rg + 2] * inv, oacc[db][4 * rg + 3] * inv);
+      }
+    if (g == 0) lse[(size_t)bh * S + my_q] = (m + fast_log2(l)) * kLn2;
+  }
+}
+
 template <typename T, int HD>
 static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v, void* o,
                       float* lse, float scale, hipStream_t stream) {
@@ -221,6 +509,18 @@ static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v
                      scale * kLog2e);
 }
 
+template <int HD>
+static void fwd_pipe(const Dims& d, const void* q, const void* k, const void* v, void* o,
+                     float* lse, float scale, hipStream_t stream) {
+  using P = FwdPipe<HD>;
+  const int nqt = (d.S + P::BM - 1) / P::BM;
+  const int BH = d.B * d.H;
+  dim3 grid((unsigned)(nqt * BH)), block(P::NT);
+  hipLaunchKernelGGL((attn_fwd_pipe_kernel<HD>), grid, block, 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, d.S, d.H,
+                     d.Hkv, nqt, BH, scale * kLog2e);
+}
+
 void launch_fwd(int dtype, const Dims& d, const void* q, const void* k, const void* v, void* o,
                 float* lse, float scale, hipStream_t stream) {
   if (dtype == 0) {
@@ -228,9 +528,9 @@ void launch_fwd(int dtype, const Dims& d, const void* q, const void* k, const vo
     else if (d.hd == 32) fwd_typed<float, 32>(d, q, k, v, o, lse, scale, stream);
     else fwd_typed<float, 64>(d, q, k, v, o, lse, scale, stream);
   } else {
-    if (d.hd == 16) fwd_typed<bf16, 16>(d, q, k, v, o, lse, scale, stream);
-    else if (d.hd == 32) fwd_typed<bf16, 32>(d, q, k, v, o, lse, scale, stream);
-    else fwd_typed<bf16, 64>(d, q, k, v, o, lse, scale, stream);
+    if (d.hd == 16) fwd_pipe<16>(d, q, k, v, o, lse, scale, stream);
+    else if (d.hd == 32) fwd_pipe<32>(d, q, k, v, o, lse, scale, stream);
+    else fwd_pipe<64>(d, q, k, v, o, lse, scale, stream);
   }
 }
 

@@ -117,6 +117,37 @@ def test_unshaped_inputs_and_other_scale(ref):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rising_scores(dtype, ref):
+    """Scores that rise along the key axis far past the first block's maximum
+    (by ~150 log2 units at the end), on every other query row: the kernels
+    must renew each row's softmax reference (or recompute the row exactly)
+    without overflow, and rows with flat scores in the same waves must be
+    unaffected.  For bf16 only the forward outputs are compared: these rows put
+    almost all weight on one key, so D = rowsum(dO * o) nearly cancels dP and
+    the bf16 rounding of o (which the backward reads) dominates dS."""
+    B, S, Hq, Hkv, hd = 1, 300, 2, 1, 64
+    rng = np.random.default_rng(4242)
+    e = np.zeros(hd, np.float32)
+    e[0] = 1.0
+    amp = np.where(np.arange(S) % 2 == 0, 4.0, 0.01).astype(np.float32)
+    q = (amp[:, None] * e[None, :] + 0.05 * rng.standard_normal((S, hd))).astype(np.float32)
+    k = (0.7 * np.arange(S, dtype=np.float32)[:, None] * e[None, :]
+         + 0.05 * rng.standard_normal((S, hd))).astype(np.float32)
+    arrs = {"q": np.broadcast_to(q, (B, Hq, S, hd)).copy(),
+            "k": np.broadcast_to(k, (B, Hkv, S, hd)).copy(),
+            "v": rng.standard_normal((B, Hkv, S, hd)).astype(np.float32),
+            "dO": rng.standard_normal((B, Hq, S, hd)).astype(np.float32)}
+    if dtype == "bf16":
+        arrs = {n: inputs.bf16_round(a) for n, a in arrs.items()}
+    scale = 1.0 / np.sqrt(hd)
+    gpu = H.gpu_run(arrs, dtype, scale)
+    r = ref.run(arrs["q"], arrs["k"], arrs["v"], arrs["dO"], scale=scale)
+    names = H.NAMES if dtype == "f32" else ("o", "lse")
+    H.compare(gpu, r, dtype, f"rising scores {dtype}", names=names,
+              terms=H.term_sizes(arrs, scale))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_long_sequence_prefix_and_identities(dtype, ref):
     """S = 8192: rows < t of o, lse, dq against the oracle on the first t
     positions; dk/dv by the exact identities sum_j dv_j = sum_i dO_i and
