@@ -42,9 +42,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "98395f75ab380bd3", "read": 110.41e6, "write": 67.11e6},
-    "dq": {"src": "af1aaccff695fcd4", "read": 99.65e6, "write": 34.08e6},
-    "fwd": {"src": "13b5dd9a44275b7d", "read": 61.76e6, "write": 17.30e6},
+    "dkdv": {"src": "f53c24f3649cf9c8", "read": 90.48e6, "write": 67.61e6},
+    "dq": {"src": "49b93af81961c064", "read": 149.24e6, "write": 34.71e6},
+    "fwd": {"src": "c29bcd8c4f573880", "read": 61.91e6, "write": 17.30e6},
 }
 
 
