@@ -248,8 +248,10 @@ struct FwdPipe {
 
 constexpr float kHalfBlockBound = 9223372036854775808.f;  // 2^63
 
+// Four workgroups per CU (128 VGPRs): every workgroup of the long-context
+// workload is resident from the start.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_fwd_pipe_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_fwd_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, int S, int H, int Hkv, int nqt, int BH,
     float c) {
@@ -375,23 +377,21 @@ __global__ __launch_bounds__(256) void attn_fwd_pipe_kernel(
 #pragma unroll
     for (int t = 0; t < P::NC; ++t)
       vf[t] = accrow_frag<bf16, HD, 32>(tV, 0, t / P::ND, 32 * (t % P::ND), lane);
-    // A(i+1) first: the next sub-step's softmax waits for its result
-    s_nxt = zero_acc();
-#pragma unroll
-    for (int t = 0; t < P::NKS; ++t) M::mma(s_nxt, kf[t], qf[t]);
     float tsum = weights(s_cur, p_cur);
     // keep B(i) in this sub-step (it would otherwise sink next to its use in C(i))
     asm volatile("" : "+v"(p_cur[0]), "+v"(p_cur[1]), "+v"(tsum));
+    s_nxt = zero_acc();
 #pragma unroll
-    for (int t = 0; t < P::NC; ++t) M::mma(oacc[t % P::ND], vf[t], p_prev[t / P::ND]);
+    for (int t = 0; t < (P::NKS > P::NC ? P::NKS : P::NC); ++t) {
+      if (t < P::NKS) M::mma(s_nxt, kf[t], qf[t]);
+      if (t < P::NC) M::mma(oacc[t % P::ND], vf[t], p_prev[t / P::ND]);
+    }
     bad = bad || !(tsum <= kHalfBlockBound);
     l += tsum;
-    // issue order: LDS reads, A(i+1) (queued on the matrix cores), the
-    // softmax arithmetic, then C(i-1)
+    // issue order: LDS reads, then the products (queued on the matrix
+    // cores), then the softmax arithmetic
     __builtin_amdgcn_sched_group_barrier(0x100, P::NKS + 2 * P::NC, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, P::NKS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 60, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, P::NC, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, P::NKS + P::NC, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   // Step u >= 1 (sub-steps 2u-1 and 2u; J0 = (2u-1) mod 4): first copies the
