@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
             p = (qi >= my_kv && qi < S) ? p : 0.f;
           }
           s[r] = p;
-          dp[r] = p * (dp[r] - tD[ql]);  // dS
+          dp[r] = p * (dp[r] + tD[ql]);  // dS (the workspace holds -D)
         }
 #pragma unroll
         for (int ks = 0; ks < C::NAS; ++ks) {
@@ -182,9 +182,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
             aq[ks] = row_frag_lds<T, HD, C::BMQ>(tQ, li, g, ks);
             ao[ks] = row_frag_lds<T, HD, C::BMQ>(tO, li, g, ks);
           }
+          // -D of the block's rows in accumulator order: dP accumulates onto
+          // it and comes out as dP - D
+          auto neg_d = [&](int qb) {
+            f32x16 d;
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const float4 v4 = *reinterpret_cast<const float4*>(tD + 32 * qb + 8 * rg + 4 * g);
+              d[4 * rg] = v4.x;
+              d[4 * rg + 1] = v4.y;
+              d[4 * rg + 2] = v4.z;
+              d[4 * rg + 3] = v4.w;
+            }
+            return d;
+          };
+          f32x16 dnext = neg_d(0);
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
-            f32x16 s = zero_acc(), dp = zero_acc();
+            f32x16 s = zero_acc(), dp = dnext;
 #pragma unroll
             for (int ks = 0; ks < C::NKS; ++ks) {
               M::mma(s, aq[ks], kf[ks]);
@@ -203,14 +218,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
               const float4 lv = *reinterpret_cast<const float4*>(tL + 32 * qb + 8 * rg + 4 * g);
-              const float4 dv4 = *reinterpret_cast<const float4*>(tD + 32 * qb + 8 * rg + 4 * g);
-              const float lr[4] = {lv.x, lv.y, lv.z, lv.w}, dr[4] = {dv4.x, dv4.y, dv4.z, dv4.w};
+              const float lr[4] = {lv.x, lv.y, lv.z, lv.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * rg + e;
                 const float p = fast_exp2(fmaf(s[r], c, -lr[e]));
                 s[r] = p;
-                dp[r] = p * (dp[r] - dr[e]);  // dS
+                dp[r] = p * dp[r];  // dS = P (dP - D)
               }
             }
             typename M::frag pf[C::NAS], sf[C::NAS];
@@ -233,6 +247,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
                 aq[ks] = row_frag_lds<T, HD, C::BMQ>(tQ, 32 * (qb + 1) + li, g, ks);
                 ao[ks] = row_frag_lds<T, HD, C::BMQ>(tO, 32 * (qb + 1) + li, g, ks);
               }
+              dnext = neg_d(qb + 1);
             }
             __builtin_amdgcn_sched_barrier(0);
           }

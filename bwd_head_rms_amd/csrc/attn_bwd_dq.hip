@@ -8,9 +8,9 @@
 // dK/dV kernel.  Then, over the key tiles j <= i:
 //   S^T  = K . Q^T,   P^T = exp2(S^T*scale*log2e - LSE_i*log2e)   (recompute)
 //   dP^T = V . dO^T
-//   dS^T = P^T * (dP^T - D_i)
+//   dS^T = P^T * (dP^T - D_i)    (the product accumulates onto -D_i)
 //   dQ^T += K^T . dS^T          (dS feeds the product from registers)
-// and dq = scale * dQ is written in fp32.  The workspace receives D and
+// and dq = scale * dQ is written in fp32.  The workspace receives -D and
 // LSE*log2e per row ([2][B][H][S] floats) for the dK/dV kernel.  K and V tiles are copied into a
 // double-buffered LDS ring (bf16: asynchronously, straight from HBM; one
 // barrier per tile); K^T for the last product comes from the same K tile by
@@ -82,13 +82,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const float Drow = halves_sum(Dp);
   const float lse2 = q_ok ? lse[(size_t)bh * S + my_q] * kLog2e : 0.f;
   if (q_ok && g == 0) {
-    dws[(size_t)bh * S + my_q] = Drow;
+    dws[(size_t)bh * S + my_q] = -Drow;  // negated: the dk/dv kernel starts dP from it
     dws[(size_t)BH * S + (size_t)bh * S + my_q] = lse2;  // for the dk/dv kernel
   }
 
   f32x16 acc[C::ND];
 #pragma unroll
   for (int d = 0; d < C::ND; ++d) acc[d] = zero_acc();
+  // dP^T accumulates onto -D, so the product yields dP - D directly
+  f32x16 negD;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negD[r] = -Drow;
 
   const int kv_end = min(S, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       auto block = [&](const int cb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int kb0 = kv_t0 + 32 * cb;
-        f32x16 s = zero_acc(), dp = zero_acc();
+        f32x16 s = zero_acc(), dp = negD;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           M::mma(s, row_frag_lds<T, HD, C::BN>(tK, 32 * cb + li, g, ks), qf[ks]);
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
             const int kv = kb0 + acc_row(r, g);
             p = (kv <= my_q && kv < S) ? p : 0.f;
           }
-          s[r] = p * (dp[r] - Drow);  // dS^T
+          s[r] = p * dp[r];  // dS^T = P (dP - D)
         }
 #pragma unroll
         for (int ks = 0; ks < C::NAS; ++ks) {

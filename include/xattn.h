@@ -93,7 +93,7 @@ int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace xattn_bwd needs: 8*B*H*S (two floats per query
- * row: D = rowsum(dO * o) and LSE * log2(e)), O(B*H*S), never S x S.
+ * row: -D = -rowsum(dO * o) and LSE * log2(e)), O(B*H*S), never S x S.
  * Returns 0 for invalid shapes.
  */
 size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype);
@@ -122,7 +122,7 @@ int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
  * xattn_bwd_dkdv(...) with the same arguments and workspace.
  *
  * xattn_bwd_dq: writes dq [B][H][S][hd] float and stores, per query row,
- *   D = rowsum(dO * o) and LSE * log2(e) in the workspace ([2][B][H][S] float).
+ *   -D = -rowsum(dO * o) and LSE * log2(e) in the workspace ([2][B][H][S] float).
  * xattn_bwd_dkdv: writes dk, dv [B][Hkv][S][hd] float; reads both per-row
  *   values from the workspace (not lse), so it must be ordered after an
  *   xattn_bwd_dq call with the same q, o, dO, lse, shapes and workspace.
