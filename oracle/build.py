@@ -1,4 +1,5 @@
-"""Build the fp64 CPU oracle (``oracle/libxattn_ref.so``) with gcc.
+"""Build the fp64 CPU oracles (``oracle/libxattn_ref.so`` for attention,
+``oracle/libxattn_ref_norm.so`` for the QK-norm + RoPE step) with gcc.
 
 Test infrastructure: the oracle is built alongside the HIP library so that the
 checker exists wherever the product is built, but nothing on the product path
@@ -10,6 +11,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "ref_attn.c")
 LIB = os.path.join(HERE, "libxattn_ref.so")
+SRC_NORM = os.path.join(HERE, "ref_qknorm_rope.c")
+LIB_NORM = os.path.join(HERE, "libxattn_ref_norm.so")
 
 # Strict IEEE double: no fast-math, no FMA contraction, so the oracle's rounding
 # is the plain C evaluation order written in the source.
@@ -25,5 +28,10 @@ def build(src=SRC, out=LIB, extra=()):
     return out
 
 
+def build_all():
+    """Both oracle libraries; returns their paths."""
+    return build(), build(SRC_NORM, LIB_NORM)
+
+
 if __name__ == "__main__":
-    print(build())
+    print(build_all())
