@@ -9,13 +9,14 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so
 
 # Every symbol include/xattn.h declares.
 SYMBOLS = ("xattn_fwd", "xattn_bwd", "xattn_bwd_workspace_bytes", "xattn_bwd_dq",
-           "xattn_bwd_dkdv", "xattn_strerror")
+           "xattn_bwd_dkdv", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
+           "xattn_qknorm_rope_bwd", "xattn_strerror")
 
 F32, BF16 = 0, 1
 STATUS = {
     0: "XATTN_OK", 1: "XATTN_ERR_NULL", 2: "XATTN_ERR_SHAPE", 3: "XATTN_ERR_GQA",
     4: "XATTN_ERR_HEAD_DIM", 5: "XATTN_ERR_DTYPE", 6: "XATTN_ERR_WORKSPACE",
-    7: "XATTN_ERR_SCALE", 8: "XATTN_ERR_HIP", 9: "XATTN_ERR_ALIGN",
+    7: "XATTN_ERR_SCALE", 8: "XATTN_ERR_HIP", 9: "XATTN_ERR_ALIGN", 10: "XATTN_ERR_PARAM",
 }
 
 
@@ -47,6 +48,12 @@ def lib():
     L.xattn_bwd_dq.restype = i
     L.xattn_bwd_dkdv.argtypes = [vp] * 7 + [i, i, i, i, i, f, i, vp, sz, vp]
     L.xattn_bwd_dkdv.restype = i
+    L.xattn_qknorm_rope_fwd.argtypes = [vp, vp, vp, i, i, i, i, f, f, i, vp]
+    L.xattn_qknorm_rope_fwd.restype = i
+    L.xattn_qknorm_rope_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    L.xattn_qknorm_rope_bwd_workspace_bytes.restype = sz
+    L.xattn_qknorm_rope_bwd.argtypes = [vp] * 5 + [i, i, i, i, f, f, i, vp, sz, vp]
+    L.xattn_qknorm_rope_bwd.restype = i
     L.xattn_strerror.argtypes = [i]
     L.xattn_strerror.restype = ctypes.c_char_p
     _lib = L

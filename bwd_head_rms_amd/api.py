@@ -111,3 +111,45 @@ class CausalAttention(torch.autograd.Function):
 
 def causal_attention(q, k, v, scale=None):
     return CausalAttention.apply(q, k, v, scale)
+
+
+def qknorm_rope_fwd(x, w, eps=1e-6, rope_base=10000.0, out=None):
+    """Per-head RMS QK-norm + rotary embedding.  x [B,S,H,hd] (fp32 or bf16,
+    token-major), w [hd] fp32.  Returns out [B,H,S,hd] in x's dtype (head-major)."""
+    if x.dim() != 4:
+        raise XattnError(2, "x must be 4-D [B, S, heads, hd]")
+    B, S, H, hd = x.shape
+    _check_tensor(x, "x", (B, S, H, hd), x.dtype)
+    _check_tensor(w, "w", (hd,), torch.float32)
+    out = torch.empty((B, H, S, hd), dtype=x.dtype, device=x.device) if out is None else out
+    _check_tensor(out, "out", (B, H, S, hd), x.dtype)
+    check(lib().xattn_qknorm_rope_fwd(x.data_ptr(), w.data_ptr(), out.data_ptr(), B, S, H, hd,
+                                      float(eps), float(rope_base), _code(x), _stream(x)))
+    return out
+
+
+def qknorm_rope_workspace_bytes(B, S, H, hd):
+    return int(lib().xattn_qknorm_rope_bwd_workspace_bytes(B, S, H, hd))
+
+
+def qknorm_rope_bwd(x, w, dout, eps=1e-6, rope_base=10000.0, dx=None, dw=None, workspace=None):
+    """Backward of qknorm_rope_fwd.  dout [B,H,S,hd] fp32.  Returns fp32
+    (dx [B,S,H,hd], dw [hd])."""
+    if x.dim() != 4:
+        raise XattnError(2, "x must be 4-D [B, S, heads, hd]")
+    B, S, H, hd = x.shape
+    _check_tensor(x, "x", (B, S, H, hd), x.dtype)
+    _check_tensor(w, "w", (hd,), torch.float32)
+    _check_tensor(dout, "dout", (B, H, S, hd), torch.float32)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty((B, S, H, hd), **f32) if dx is None else dx
+    dw = torch.empty((hd,), **f32) if dw is None else dw
+    _check_tensor(dx, "dx", (B, S, H, hd), torch.float32)
+    _check_tensor(dw, "dw", (hd,), torch.float32)
+    if workspace is None:
+        workspace = torch.empty((max(1, qknorm_rope_workspace_bytes(B, S, H, hd) // 4),), **f32)
+    check(lib().xattn_qknorm_rope_bwd(x.data_ptr(), w.data_ptr(), dout.data_ptr(), dx.data_ptr(),
+                                      dw.data_ptr(), B, S, H, hd, float(eps), float(rope_base),
+                                      _code(x), workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream(x)))
+    return dx, dw

@@ -117,6 +117,52 @@ int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
                         workspace_bytes, stream);
 }
 
+namespace {
+int check_norm(int B, int S, int H, int hd, float eps, float base, int dtype) {
+  if (dtype != XATTN_F32 && dtype != XATTN_BF16) return XATTN_ERR_DTYPE;
+  if (B <= 0 || S <= 0 || H <= 0 || hd <= 0) return XATTN_ERR_SHAPE;
+  if (hd != 16 && hd != 32 && hd != 64) return XATTN_ERR_HEAD_DIM;
+  if ((int64_t)B * S * H * hd > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
+  if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(base) || !(base > 1.f))
+    return XATTN_ERR_PARAM;
+  return XATTN_OK;
+}
+}  // namespace
+
+int xattn_qknorm_rope_fwd(const void* x, const float* w, void* out, int B, int S, int H, int hd,
+                          float eps, float rope_base, int dtype, void* stream) {
+  if (!x || !w || !out) return XATTN_ERR_NULL;
+  const int rc = check_norm(B, S, H, hd, eps, rope_base, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(out)) return XATTN_ERR_ALIGN;
+  xattn::launch_qknorm_rope_fwd(dtype, xattn::NormDims{B, S, H, hd}, x, w, out, eps, rope_base,
+                                static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+size_t xattn_qknorm_rope_bwd_workspace_bytes(int B, int S, int H, int hd) {
+  if (check_norm(B, S, H, hd, 0.f, 10000.f, XATTN_F32) != XATTN_OK) return 0;
+  return sizeof(float) * (size_t)hd *
+         (size_t)xattn::qknorm_bwd_blocks((long)B * S * H, hd);
+}
+
+int xattn_qknorm_rope_bwd(const void* x, const float* w, const float* dout, float* dx, float* dw,
+                          int B, int S, int H, int hd, float eps, float rope_base, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w || !dout || !dx || !dw) return XATTN_ERR_NULL;
+  const int rc = check_norm(B, S, H, hd, eps, rope_base, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!workspace || workspace_bytes < xattn_qknorm_rope_bwd_workspace_bytes(B, S, H, hd))
+    return XATTN_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(dout) || !aligned16(dx) || !aligned16(dw) ||
+      !aligned16(workspace))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_qknorm_rope_bwd(dtype, xattn::NormDims{B, S, H, hd}, x, w, dout, dx, dw,
+                                static_cast<float*>(workspace), eps, rope_base,
+                                static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 const char* xattn_strerror(int status) {
   switch (status) {
     case XATTN_OK: return "success";
@@ -125,10 +171,11 @@ const char* xattn_strerror(int status) {
     case XATTN_ERR_GQA: return "H must be a multiple of Hkv";
     case XATTN_ERR_HEAD_DIM: return "head dimension must be 16, 32 or 64";
     case XATTN_ERR_DTYPE: return "dtype must be XATTN_F32 or XATTN_BF16";
-    case XATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than xattn_bwd_workspace_bytes()";
+    case XATTN_ERR_WORKSPACE: return "workspace is NULL or smaller than the required size";
     case XATTN_ERR_SCALE: return "scale must be positive and finite";
     case XATTN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case XATTN_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
+    case XATTN_ERR_PARAM: return "eps must be finite and >= 0, and the rope base finite and > 1";
     default: return "unknown xattn status";
   }
 }

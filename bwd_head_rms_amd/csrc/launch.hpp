@@ -23,4 +23,24 @@ void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, con
                      const float* lse, const void* dO, const float* dws, float* dk, float* dv,
                      float scale, hipStream_t stream);
 
+// Per-head RMS QK-norm + rotary embedding.  x [B][S][H][hd] (token-major),
+// out and dout [B][H][S][hd], dx [B][S][H][hd], w and dw [hd].
+struct NormDims {
+  int B, S, H, hd;
+};
+
+// Largest grid of the backward kernel: its workspace holds one fp32 row of hd
+// partial weight-gradient sums per workgroup.
+constexpr int kNormMaxBlocks = 1024;
+
+// Workgroups the backward launches for nvec = B*S*H head vectors.
+int qknorm_bwd_blocks(long nvec, int hd);
+
+void launch_qknorm_rope_fwd(int dtype, const NormDims& d, const void* x, const float* w,
+                            void* out, float eps, float base, hipStream_t stream);
+
+void launch_qknorm_rope_bwd(int dtype, const NormDims& d, const void* x, const float* w,
+                            const float* dout, float* dx, float* dw, float* ws, float eps,
+                            float base, hipStream_t stream);
+
 }  // namespace xattn

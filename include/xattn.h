@@ -76,7 +76,8 @@ typedef enum {
   XATTN_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than required */
   XATTN_ERR_SCALE = 7,      /* scale not positive and finite */
   XATTN_ERR_HIP = 8,        /* the HIP runtime rejected a kernel launch */
-  XATTN_ERR_ALIGN = 9       /* a data pointer is not 16-byte aligned */
+  XATTN_ERR_ALIGN = 9,      /* a data pointer is not 16-byte aligned */
+  XATTN_ERR_PARAM = 10      /* eps or rope base out of range (QK-norm + RoPE) */
 } xattn_status;
 
 /*
@@ -138,6 +139,51 @@ int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse
                    void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
+/*
+ * Per-head RMS QK-norm + rotary position embedding: the step that turns a q (or
+ * k) projection output into the attention input (the per-head QK-norm of the
+ * "xtrain evolution overview", section 一, row T9; RoPE with the position
+ * restarting per sequence, rows T5 and T10 and the KI-1 fix of "xtrain --
+ * Known Issues & Perf Backlog"; the head-major transpose of that fix folded
+ * into the store).  For token (b, s) and head h, x = X[b,s,h,:]:
+ *   r = sqrt(mean_d x_d^2 + eps),  y = w * x / r,
+ *   out[b,h,s,i]        = y_i cos t_i - y_{i+hd/2} sin t_i
+ *   out[b,h,s,i+hd/2]   = y_{i+hd/2} cos t_i + y_i sin t_i,
+ *   t_i = s * rope_base^(-2i/hd),  i < hd/2.
+ *   x   [B][S][H][hd] in `dtype` (token-major, as the projection writes it)
+ *   w   [hd] float (one weight per head dimension, shared by all heads)
+ *   out [B][H][S][hd] in `dtype` (head-major: ready for xattn_fwd)
+ * Norm arithmetic is fp32; bf16 outputs are rounded to nearest-even.
+ * Supported: hd in {16, 32, 64}; B*S*H*hd < 2^31; eps finite >= 0; rope_base
+ * finite > 1; 16-byte aligned pointers.  Same ownership, stream and error
+ * rules as xattn_fwd.  Returns an xattn_status.
+ */
+int xattn_qknorm_rope_fwd(const void* x, const float* w, void* out, int B, int S, int H, int hd,
+                          float eps, float rope_base, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace xattn_qknorm_rope_bwd needs: hd floats per
+ * workgroup of its fixed grid (at most 1024 workgroups, so at most 256 KB).
+ * Returns 0 for invalid shapes.
+ */
+size_t xattn_qknorm_rope_bwd_workspace_bytes(int B, int S, int H, int hd);
+
+/*
+ * Backward of xattn_qknorm_rope_fwd for an upstream gradient dout:
+ *   g = R(t)^T dout (the rotation transposed),  xh = x / r,  gxh = w * g,
+ *   dx = (gxh - xh * mean_d(xh * gxh)) / r,   dw = sum over all (b, s, h) of xh * g.
+ *   x    [B][S][H][hd] in `dtype`, w [hd] float          (inputs, as in the forward)
+ *   dout [B][H][S][hd] float (e.g. xattn_bwd's dq or dk)  (input)
+ *   dx   [B][S][H][hd] float, dw [hd] float               (outputs, overwritten)
+ *   workspace: device scratch of at least xattn_qknorm_rope_bwd_workspace_bytes
+ *   bytes, 16-byte aligned; its contents on entry do not matter.
+ * dw is summed in a fixed order (no atomics): bitwise reproducible.  Two
+ * kernels are enqueued in order on `stream`.  Returns an xattn_status.
+ */
+int xattn_qknorm_rope_bwd(const void* x, const float* w, const float* dout, float* dx, float* dw,
+                          int B, int S, int H, int hd, float eps, float rope_base, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 const char* xattn_strerror(int status);
 
 #ifdef __cplusplus

@@ -145,3 +145,59 @@ def test_product_package_never_imports_the_oracle():
             text = open(path).read()
             assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), path
             assert "xattn_ref" not in text and "ref_attn" not in text, path
+
+
+# -- per-head RMS QK-norm + RoPE -----------------------------------------------
+PARAM = 10
+
+
+def nfwd(L, x=P, w=P, out=P, B=1, S=4, H=2, hd=16, eps=1e-6, base=10000.0, dtype=0):
+    return L.xattn_qknorm_rope_fwd(x, w, out, B, S, H, hd, eps, base, dtype, None)
+
+
+def nbwd(L, ws=P, ws_bytes=None, B=1, S=4, H=2, hd=16, eps=1e-6, base=10000.0, dtype=0, **ptrs):
+    p = {n: P for n in ("x", "w", "dout", "dx", "dw")}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = L.xattn_qknorm_rope_bwd_workspace_bytes(B, S, H, hd)
+    return L.xattn_qknorm_rope_bwd(p["x"], p["w"], p["dout"], p["dx"], p["dw"], B, S, H, hd, eps,
+                                   base, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["x", "w", "out"])
+def test_norm_fwd_null_pointer(L, name):
+    assert nfwd(L, **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("name", ["x", "w", "dout", "dx", "dw"])
+def test_norm_bwd_null_pointer(L, name):
+    assert nbwd(L, **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), SHAPE), (dict(S=0), SHAPE), (dict(H=-1), SHAPE), (dict(hd=0), SHAPE),
+    (dict(hd=48), HEAD_DIM), (dict(hd=128), HEAD_DIM), (dict(dtype=2), DTYPE),
+    (dict(eps=-1e-6), PARAM), (dict(eps=float("nan")), PARAM), (dict(eps=float("inf")), PARAM),
+    (dict(base=1.0), PARAM), (dict(base=0.0), PARAM), (dict(base=float("inf")), PARAM),
+    (dict(B=1 << 15, S=1 << 12, H=16, hd=64), SHAPE),
+    (dict(x=P + 8), ALIGN), (dict(out=P + 4), ALIGN), (dict(w=P + 2), ALIGN)])
+def test_norm_fwd_rejects(L, kw, status):
+    assert nfwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=0), WORKSPACE), (dict(hd=32), WORKSPACE),
+    (dict(eps=-1.0), PARAM), (dict(dtype=-1), DTYPE), (dict(dx=P + 8), ALIGN),
+    (dict(dout=P + 4), ALIGN), (dict(ws=P + 8), ALIGN)])
+def test_norm_bwd_rejects(L, kw, status):
+    if kw.get("hd") == 32:  # workspace sized for hd 16 is too small for hd 32
+        kw = dict(kw, ws_bytes=L.xattn_qknorm_rope_bwd_workspace_bytes(1, 4, 2, 16))
+    assert nbwd(L, **kw) == status
+
+
+def test_norm_workspace_bytes(L):
+    f = L.xattn_qknorm_rope_bwd_workspace_bytes
+    assert f(1, 4, 2, 16) == 4 * 16 * 1                     # one workgroup
+    assert f(4, 2048, 16, 64) == 4 * 64 * 1024               # capped grid
+    assert f(0, 4, 2, 16) == 0 and f(1, 4, 2, 48) == 0
+    assert L.xattn_strerror(PARAM).decode().startswith("eps")
