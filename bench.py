@@ -17,6 +17,12 @@ dq kernel 6*hd*nnz (S, dP, dS.K), dk/dv kernel 8*hd*nnz (S, dP, P^T.dO, dS^T.Q).
 The CPU baseline times the fp64 oracle on a bounded sample of the same
 workload (whole (batch, kv head) units) on the host's cores, rank 0, N = 1.
 
+`next_rows` reports the step before attention, the per-head RMS QK-norm +
+RoPE forward and backward, on the long-context workload's q input, against
+MI355X's HBM bandwidth (algorithmic bytes: fwd reads x and writes out; bwd
+reads x and the fp32 upstream gradient and writes the fp32 dx).  It is not
+part of the timed attention step.
+
 Prints ONE JSON line.
 """
 import argparse
@@ -32,6 +38,7 @@ if ROOT not in sys.path:
 
 METRIC = "causal attn fwd+bwd TFLOP/s & % MFMA peak (B16 S256 H12 hd32; B4 S2048 hd64)"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 HBM_GBS = 8000.0
 
 KERNEL_FILES = {"fwd": "attn_fwd.hip", "dq": "attn_bwd_dq.hip", "dkdv": "attn_bwd_dkdv.hip"}
@@ -141,6 +148,67 @@ def run_gpu(w, steps, warmup):
             "device": torch.cuda.get_device_name(dev)}
 
 
+def norm_bytes(w):
+    """Algorithmic HBM bytes of the QK-norm + RoPE step on the q input of `w`:
+    fwd reads x and writes out (input dtype); bwd reads x (input dtype) and
+    dout (fp32) and writes dx (fp32).  The weight, dw and the workspace are
+    negligible and not counted."""
+    n = w.B * w.S * w.H * w.hd
+    e = 2 if w.dtype == "bf16" else 4
+    return {"fwd": 2 * e * n, "bwd": (e + 8) * n}
+
+
+def run_norm(w, steps, warmup):
+    """Time xattn_qknorm_rope_fwd / _bwd on the q input of workload `w`:
+    x [B, S, H, hd] in the workload dtype, dout fp32, inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    from bwd_head_rms_amd import _lib, inputs
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(w.seed)
+    x = inputs.to_torch(rng.standard_normal((w.B, w.S, w.H, w.hd)).astype(np.float32), w.dtype, dev)
+    wt = torch.from_numpy((1.0 + 0.25 * rng.standard_normal(w.hd)).astype(np.float32)).to(dev)
+    g = torch.from_numpy(rng.standard_normal((w.B, w.H, w.S, w.hd)).astype(np.float32)).to(dev)
+    out = torch.empty((w.B, w.H, w.S, w.hd), dtype=x.dtype, device=dev)
+    dx = torch.empty((w.B, w.S, w.H, w.hd), dtype=torch.float32, device=dev)
+    dw = torch.empty((w.hd,), dtype=torch.float32, device=dev)
+    wsb = int(L.xattn_qknorm_rope_bwd_workspace_bytes(w.B, w.S, w.H, w.hd))
+    ws = torch.empty((max(1, wsb // 4),), dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    code = _lib.BF16 if w.dtype == "bf16" else _lib.F32
+    dims = (w.B, w.S, w.H, w.hd, 1e-6, 10000.0, code)
+
+    def fwd():
+        _lib.check(L.xattn_qknorm_rope_fwd(x.data_ptr(), wt.data_ptr(), out.data_ptr(), *dims, sh))
+
+    def bwd():
+        _lib.check(L.xattn_qknorm_rope_bwd(x.data_ptr(), wt.data_ptr(), g.data_ptr(), dx.data_ptr(),
+                                           dw.data_ptr(), *dims, ws.data_ptr(), wsb, sh))
+
+    res = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps  # ms
+    nb = norm_bytes(w)
+    roof = {k: {"achieved": round(nb[k] / (res[k] / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(nb[k] / (res[k] / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "alg_bytes": nb[k]} for k in res}
+    return {"workload": f"q input of {w.name}: x [{w.B},{w.S},{w.H},{w.hd}] {w.dtype}, dout fp32",
+            "fwd_us": round(res["fwd"] * 1e3, 2), "bwd_us": round(res["bwd"] * 1e3, 2),
+            "roofline": {"bound": "hbm", **roof}}
+
+
 def cpu_baseline(w, budget_units=None):
     """Time the fp64 oracle on whole (batch, kv head) units of the workload."""
     import numpy as np
@@ -187,6 +255,10 @@ def main():
     ap.add_argument("--workload", default=None, help="name from bwd_head_rms_amd.inputs.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the QK-norm + RoPE step (reported under 'next_rows')")
+    ap.add_argument("--norm-only", action="store_true",
+                    help="only time the QK-norm + RoPE step (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (for counter calibration)")
     args = ap.parse_args()
@@ -202,6 +274,9 @@ def main():
 
     from bwd_head_rms_amd import inputs
     w = inputs.WORKLOADS[args.workload or inputs.LONG_CONTEXT]
+    if args.norm_only:
+        print(json.dumps({"qknorm_rope": run_norm(w, args.steps, args.warmup)}), flush=True)
+        return
     fl = counted_flops(w)
     r = run_gpu(w, args.steps, args.warmup)
     sec = r["ms_per_step"] / 1e3
@@ -247,6 +322,8 @@ def main():
                             "ms_per_step": round(r2["ms_per_step"], 5),
                             "tokens_per_s": round(w2.B * w2.S / s2, 1),
                             "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in r2["kernel_ms"].items()}}
+    if not args.no_next:
+        out["next_rows"] = {"qknorm_rope": run_norm(w, args.steps, args.warmup)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)

@@ -12,8 +12,8 @@
 // Both kernels are HBM-bound elementwise passes: one thread owns four rotation
 // pairs (8 of a head vector's hd values: two 8- or 16-byte loads), hd/8 adjacent
 // threads own one head vector and reduce its sums with cross-lane exchanges.
-// Angles are formed in fp64 and reduced to [-pi, pi] before an fp32 sincos, so
-// positions up to 2^31 keep full fp32 accuracy.
+// Angles are formed in fp64 (in turns) and reduced to [-1/2, 1/2] turn before the
+// hardware sine and cosine, so positions up to 2^31 keep full fp32 accuracy.
 //
 // Backward, per head vector, with g = dOut (fp32, head-major):
 //   gy = R(theta)^T g,  xh = x / r,  gxh = w * gy,
@@ -21,7 +21,7 @@
 //   dw = sum over every (b, s, h) of xh * gy         (fp32)
 // dw is summed deterministically: each workgroup of a fixed grid walks a fixed
 // set of vectors, reduces its threads' partial sums in a fixed order into one
-// workspace row, and a one-workgroup kernel adds the rows in order.
+// workspace row, and a second kernel adds the rows in a fixed order.
 #include <type_traits>
 
 #include "attn_device.hpp"
@@ -38,12 +38,21 @@ struct NormCfg {
 };
 
 constexpr double kTwoPi = 6.283185307179586;
+constexpr long kNormFwdBlocks = 2048;  // forward grid cap: each thread then walks several vectors
 
-// cos and sin of s * inv_freq, with the angle reduced to [-pi, pi] in fp64
-__device__ __forceinline__ void rope_cs(int s, double inv_freq, float& c, float& sn) {
-  const double a = (double)s * inv_freq;
-  const double red = a - kTwoPi * rint(a * (1.0 / kTwoPi));
-  sincosf((float)red, &sn, &c);
+// cos and sin of s * inv_freq: the angle, in turns (inv_freq is given in turns
+// per position), is reduced to [-1/2, 1/2] in fp64, then the hardware sine and
+// cosine (which take turns) finish in fp32
+__device__ __forceinline__ void rope_cs(int s, double turns_per_pos, float& c, float& sn) {
+  const double a = (double)s * turns_per_pos;
+  const float red = (float)(a - rint(a));
+  sn = __builtin_amdgcn_sinf(red);
+  c = __builtin_amdgcn_cosf(red);
+}
+
+// rotation frequency of pair i, in turns per position: base^(-2i/hd) / (2 pi)
+__device__ __forceinline__ double turns_per_pos(int i, int hd, double log2_base) {
+  return exp2(-2.0 * i / hd * log2_base) * (1.0 / kTwoPi);
 }
 
 // four consecutive values of a row (bf16 or float) as float
@@ -72,38 +81,45 @@ __global__ __launch_bounds__(256) void qknorm_rope_fwd_kernel(const T* __restric
                                                               long nvec, float eps,
                                                               double log2_base) {
   using C = NormCfg<HD>;
-  const long t = (long)blockIdx.x * C::NT + threadIdx.x;
-  const long v = t / C::TPV;  // head vector: (b * S + s) * H + h
-  const int j = (int)(t % C::TPV);
-  if (v >= nvec) return;  // whole vectors only: nvec * TPV threads are live
-  const int h = (int)(v % H);
-  const long bs = v / H;
-  const int s = (int)(bs % S);
-  const long b = bs / S;
+  const int j = threadIdx.x % C::TPV;  // fixed: the grid stride is a multiple of TPV
   const int i0 = 4 * j;
-
-  const T* xv = x + v * HD;
-  const float4 a = load4(xv + i0), c4 = load4(xv + C::HALF + i0);
-  const float x1[4] = {a.x, a.y, a.z, a.w}, x2[4] = {c4.x, c4.y, c4.z, c4.w};
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
-  ss = vec_sum<C::TPV>(ss);
-  const float rinv = 1.f / sqrtf(ss * (1.f / HD) + eps);
-
-  float o1[4], o2[4];
+  double fr[4];
+  float w1[4], w2[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int i = i0 + e;
-    float cs, sn;
-    rope_cs(s, exp2(-2.0 * i / HD * log2_base), cs, sn);
-    const float y1 = w[i] * (x1[e] * rinv), y2 = w[i + C::HALF] * (x2[e] * rinv);
-    o1[e] = y1 * cs - y2 * sn;
-    o2[e] = y2 * cs + y1 * sn;
+    fr[e] = turns_per_pos(i0 + e, HD, log2_base);
+    w1[e] = w[i0 + e];
+    w2[e] = w[C::HALF + i0 + e];
   }
-  T* ov = out + ((b * H + h) * S + s) * HD;
-  store4<T>(ov + i0, o1[0], o1[1], o1[2], o1[3]);
-  store4<T>(ov + C::HALF + i0, o2[0], o2[1], o2[2], o2[3]);
+  const long stride = (long)gridDim.x * C::NT / C::TPV;  // vectors per grid pass
+  // whole vectors only: a vector's TPV threads are adjacent lanes
+  for (long v = ((long)blockIdx.x * C::NT + threadIdx.x) / C::TPV; v < nvec; v += stride) {
+    const int h = (int)(v % H);
+    const long bs = v / H;
+    const int s = (int)(bs % S);
+    const long b = bs / S;
+    const T* xv = x + v * HD;
+    const float4 a = load4(xv + i0), c4 = load4(xv + C::HALF + i0);
+    const float x1[4] = {a.x, a.y, a.z, a.w}, x2[4] = {c4.x, c4.y, c4.z, c4.w};
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss += x1[e] * x1[e] + x2[e] * x2[e];
+    ss = vec_sum<C::TPV>(ss);
+    const float rinv = 1.f / sqrtf(ss * (1.f / HD) + eps);
+
+    float o1[4], o2[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float cs, sn;
+      rope_cs(s, fr[e], cs, sn);
+      const float y1 = w1[e] * (x1[e] * rinv), y2 = w2[e] * (x2[e] * rinv);
+      o1[e] = y1 * cs - y2 * sn;
+      o2[e] = y2 * cs + y1 * sn;
+    }
+    T* ov = out + ((b * H + h) * S + s) * HD;
+    store4<T>(ov + i0, o1[0], o1[1], o1[2], o1[3]);
+    store4<T>(ov + C::HALF + i0, o2[0], o2[1], o2[2], o2[3]);
+  }
 }
 
 template <typename T, int HD>
@@ -119,7 +135,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
   float w1[4], w2[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    inv[e] = exp2(-2.0 * (i0 + e) / HD * log2_base);
+    inv[e] = turns_per_pos(i0 + e, HD, log2_base);
     w1[e] = w[i0 + e];
     w2[e] = w[C::HALF + i0 + e];
   }
@@ -183,15 +199,27 @@ __global__ __launch_bounds__(256) void qknorm_rope_bwd_kernel(
   }
 }
 
-// dw[d] = sum over workgroups (ascending) of their partial rows
+// dw[d] = sum of the workgroups' partial rows in a fixed order: one workgroup
+// per dimension d; thread t adds rows t, t + 256, t + 512, ... (independent
+// loads), then a fixed pairwise tree over the 256 thread sums
+constexpr int kReduceThreads = 256;
+
 template <int HD>
-__global__ __launch_bounds__(64) void qknorm_dw_reduce_kernel(const float* __restrict__ part,
-                                                              int nblk, float* __restrict__ dw) {
-  const int d = threadIdx.x;
-  if (d >= HD) return;
+__global__ __launch_bounds__(kReduceThreads) void qknorm_dw_reduce_kernel(
+    const float* __restrict__ part, int nblk, float* __restrict__ dw) {
+  __shared__ float t_sum[kReduceThreads];
+  const int d = blockIdx.x, t = threadIdx.x;
   float sum = 0.f;
-  for (int k = 0; k < nblk; ++k) sum += part[(size_t)k * HD + d];
-  dw[d] = sum;
+#pragma unroll 4
+  for (int k = t; k < nblk; k += kReduceThreads) sum += part[(size_t)k * HD + d];
+  t_sum[t] = sum;
+  __syncthreads();
+#pragma unroll
+  for (int n = kReduceThreads / 2; n >= 1; n /= 2) {
+    if (t < n) t_sum[t] += t_sum[t + n];
+    __syncthreads();
+  }
+  if (t == 0) dw[d] = t_sum[0];
 }
 
 int qknorm_bwd_blocks(long nvec, int hd) {
@@ -205,7 +233,8 @@ static void norm_fwd_typed(const NormDims& d, const void* x, const float* w, voi
                            float eps, float base, hipStream_t stream) {
   using C = NormCfg<HD>;
   const long nvec = (long)d.B * d.S * d.H;
-  const long blocks = (nvec * C::TPV + C::NT - 1) / C::NT;
+  const long need = (nvec * C::TPV + C::NT - 1) / C::NT;
+  const long blocks = need < kNormFwdBlocks ? need : kNormFwdBlocks;
   hipLaunchKernelGGL((qknorm_rope_fwd_kernel<T, HD>), dim3((unsigned)blocks), dim3(C::NT), 0,
                      stream, (const T*)x, w, (T*)out, d.S, d.H, nvec, eps, log2((double)base));
 }
@@ -219,7 +248,8 @@ static void norm_bwd_typed(const NormDims& d, const void* x, const float* w, con
   const int blocks = qknorm_bwd_blocks(nvec, HD);
   hipLaunchKernelGGL((qknorm_rope_bwd_kernel<T, HD>), dim3(blocks), dim3(C::NT), 0, stream,
                      (const T*)x, w, dout, dx, ws, d.S, d.H, nvec, eps, log2((double)base));
-  hipLaunchKernelGGL((qknorm_dw_reduce_kernel<HD>), dim3(1), dim3(64), 0, stream, ws, blocks, dw);
+  hipLaunchKernelGGL((qknorm_dw_reduce_kernel<HD>), dim3(HD), dim3(kReduceThreads), 0, stream, ws,
+                     blocks, dw);
 }
 
 void launch_qknorm_rope_fwd(int dtype, const NormDims& d, const void* x, const float* w,
