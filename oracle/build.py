@@ -1,5 +1,6 @@
 """Build the fp64 CPU oracles (``oracle/libxattn_ref.so`` for attention,
-``oracle/libxattn_ref_norm.so`` for the QK-norm + RoPE step) with gcc.
+``oracle/libxattn_ref_norm.so`` for the QK-norm + RoPE step,
+``oracle/libxattn_ref_decode.so`` for decode attention) with gcc.
 
 Test infrastructure: the oracle is built alongside the HIP library so that the
 checker exists wherever the product is built, but nothing on the product path
@@ -13,6 +14,8 @@ SRC = os.path.join(HERE, "ref_attn.c")
 LIB = os.path.join(HERE, "libxattn_ref.so")
 SRC_NORM = os.path.join(HERE, "ref_qknorm_rope.c")
 LIB_NORM = os.path.join(HERE, "libxattn_ref_norm.so")
+SRC_DEC = os.path.join(HERE, "ref_decode.c")
+LIB_DEC = os.path.join(HERE, "libxattn_ref_decode.so")
 
 # Strict IEEE double: no fast-math, no FMA contraction, so the oracle's rounding
 # is the plain C evaluation order written in the source.
@@ -29,8 +32,8 @@ def build(src=SRC, out=LIB, extra=()):
 
 
 def build_all():
-    """Both oracle libraries; returns their paths."""
-    return build(), build(SRC_NORM, LIB_NORM)
+    """Every oracle library; returns their paths."""
+    return build(), build(SRC_NORM, LIB_NORM), build(SRC_DEC, LIB_DEC)
 
 
 if __name__ == "__main__":
