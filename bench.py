@@ -20,8 +20,11 @@ workload (whole (batch, kv head) units) on the host's cores, rank 0, N = 1.
 `next_rows` reports the step before attention, the per-head RMS QK-norm +
 RoPE forward and backward, on the long-context workload's q input, against
 MI355X's HBM bandwidth (algorithmic bytes: fwd reads x and writes out; bwd
-reads x and the fp32 upstream gradient and writes the fp32 dx).  It is not
-part of the timed attention step.
+reads x and the fp32 upstream gradient and writes the fp32 dx), and decode
+attention (one new query per sequence and head against a K/V cache) on a
+32768-position bf16 cache and on the long-context workload's last row, against
+the same bandwidth (algorithmic bytes: the cached K and V once, q, o and lse).
+Neither is part of the timed attention step.
 
 Prints ONE JSON line.
 """
@@ -247,6 +250,57 @@ def calibrate_copy(nbytes, reps=5):
                       "reps": reps}), flush=True)
 
 
+def decode_bytes(wd):
+    """Algorithmic HBM bytes of one decode step: K and V of every cached
+    position once, q and o (input dtype), lse (fp32).  The chunk partials in the
+    workspace are overhead and not counted."""
+    e = 2 if wd.dtype == "bf16" else 4
+    return 2 * wd.B * wd.Hkv * wd.T * wd.hd * e + 2 * wd.B * wd.H * wd.hd * e + 4 * wd.B * wd.H
+
+
+def run_decode(wd, steps, warmup):
+    """Time xattn_decode on decode workload `wd` (inputs resident in HBM):
+    `steps` back-to-back calls between HIP events on the launch stream."""
+    import torch
+
+    from bwd_head_rms_amd import _lib, inputs
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    a = inputs.generate_decode(wd)
+    t = {n: inputs.to_torch(x, wd.dtype, dev) for n, x in a.items()}
+    del a
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((wd.B, wd.H), dtype=torch.float32, device=dev)
+    wsb = int(L.xattn_decode_workspace_bytes(wd.B, wd.T, wd.H, wd.Hkv, wd.hd))
+    ws = torch.empty((max(1, wsb // 4),), dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    code = _lib.BF16 if wd.dtype == "bf16" else _lib.F32
+
+    def call():
+        _lib.check(L.xattn_decode(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(), None,
+                                  o.data_ptr(), lse.data_ptr(), wd.B, wd.T, wd.H, wd.Hkv, wd.hd,
+                                  wd.scale, code, ws.data_ptr(), wsb, sh))
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nb = decode_bytes(wd)
+    gbs = nb / (ms / 1e3) / 1e9
+    return {"workload": wd.name, "B": wd.B, "T": wd.T, "H": wd.H, "Hkv": wd.Hkv, "hd": wd.hd,
+            "dtype": wd.dtype, "us": round(ms * 1e3, 2),
+            "tokens_per_s": round(wd.B / (ms / 1e3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBPS, 4), "alg_bytes": nb}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,9 +310,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the QK-norm + RoPE step (reported under 'next_rows')")
+                    help="skip the QK-norm + RoPE step and decode attention ('next_rows')")
     ap.add_argument("--norm-only", action="store_true",
                     help="only time the QK-norm + RoPE step (for profiling its kernels)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time decode attention (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (for counter calibration)")
     args = ap.parse_args()
@@ -276,6 +332,10 @@ def main():
     w = inputs.WORKLOADS[args.workload or inputs.LONG_CONTEXT]
     if args.norm_only:
         print(json.dumps({"qknorm_rope": run_norm(w, args.steps, args.warmup)}), flush=True)
+        return
+    if args.decode_only:
+        wd = inputs.DECODE_WORKLOADS[inputs.DECODE_BENCH]
+        print(json.dumps({"decode": run_decode(wd, args.steps, args.warmup)}), flush=True)
         return
     fl = counted_flops(w)
     r = run_gpu(w, args.steps, args.warmup)
@@ -323,7 +383,13 @@ def main():
                             "tokens_per_s": round(w2.B * w2.S / s2, 1),
                             "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in r2["kernel_ms"].items()}}
     if not args.no_next:
-        out["next_rows"] = {"qknorm_rope": run_norm(w, args.steps, args.warmup)}
+        out["next_rows"] = {
+            "qknorm_rope": run_norm(w, args.steps, args.warmup),
+            "decode": run_decode(inputs.DECODE_WORKLOADS[inputs.DECODE_BENCH], args.steps,
+                                 args.warmup),
+            "decode_long_context_last_row": run_decode(
+                inputs.DECODE_WORKLOADS["decode_long_b4_t2048_h16_hd64_bf16"], args.steps,
+                args.warmup)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)

@@ -153,3 +153,40 @@ def qknorm_rope_bwd(x, w, dout, eps=1e-6, rope_base=10000.0, dx=None, dw=None, w
                                       _code(x), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), _stream(x)))
     return dx, dw
+
+
+def decode_workspace_bytes(B, T, H, Hkv, hd):
+    return int(lib().xattn_decode_workspace_bytes(B, T, H, Hkv, hd))
+
+
+def decode(q, k, v, lens=None, scale=None, o=None, lse=None, workspace=None):
+    """Decode attention: one query per (sequence, head) against the K/V cache.
+
+    q [B,H,hd]; k, v [B,Hkv,T,hd] (fp32 or bf16; T = cache capacity);
+    lens [B] int32 on the device (positions held per sequence) or None (all T).
+    Returns (o [B,H,hd] in q's dtype, lse [B,H] fp32).
+    """
+    if q.dim() != 3 or k.dim() != 4:
+        raise XattnError(2, "q must be [B, H, hd] and k, v [B, Hkv, T, hd]")
+    B, H, hd = q.shape
+    Hkv, T = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check_tensor(q, "q", (B, H, hd), q.dtype)
+    _check_tensor(k, "k", (B, Hkv, T, hd), q.dtype)
+    _check_tensor(v, "v", (B, Hkv, T, hd), q.dtype)
+    if lens is not None:
+        _check_tensor(lens, "lens", (B,), torch.int32)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor(o, "o", (B, H, hd), q.dtype)
+    _check_tensor(lse, "lse", (B, H), torch.float32)
+    need = decode_workspace_bytes(B, T, H, Hkv, hd)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need // 4,), dtype=torch.float32, device=q.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib().xattn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             None if lens is None else lens.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), B, T, H, Hkv, hd, scale, _code(q), wptr, wbytes,
+                             _stream(q)))
+    return o, lse

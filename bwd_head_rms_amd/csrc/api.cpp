@@ -163,6 +163,43 @@ int xattn_qknorm_rope_bwd(const void* x, const float* w, const float* dout, floa
   return launch_status();
 }
 
+namespace {
+int check_decode(int B, int T, int H, int Hkv, int hd, float scale, int dtype) {
+  if (dtype != XATTN_F32 && dtype != XATTN_BF16) return XATTN_ERR_DTYPE;
+  if (B <= 0 || T <= 0 || H <= 0 || Hkv <= 0 || hd <= 0) return XATTN_ERR_SHAPE;
+  if (H % Hkv != 0) return XATTN_ERR_GQA;
+  if (hd != 16 && hd != 32 && hd != 64) return XATTN_ERR_HEAD_DIM;
+  if ((int64_t)T * hd > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
+  if (T > xattn::kDecodeMaxT) return XATTN_ERR_SHAPE;
+  if ((int64_t)B * H * hd > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
+  if (xattn::decode_plan(B, T, H, Hkv, hd).blocks > std::numeric_limits<int32_t>::max())
+    return XATTN_ERR_SHAPE;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return XATTN_ERR_SCALE;
+  return XATTN_OK;
+}
+}  // namespace
+
+size_t xattn_decode_workspace_bytes(int B, int T, int H, int Hkv, int hd) {
+  if (check_decode(B, T, H, Hkv, hd, 1.f, XATTN_F32) != XATTN_OK) return 0;
+  return xattn::decode_plan(B, T, H, Hkv, hd).part_bytes;
+}
+
+int xattn_decode(const void* q, const void* k, const void* v, const int* lens, void* o,
+                 float* lse, int B, int T, int H, int Hkv, int hd, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return XATTN_ERR_NULL;
+  const int rc = check_decode(B, T, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  const size_t need = xattn::decode_plan(B, T, H, Hkv, hd).part_bytes;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return XATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      (need > 0 && !aligned16(workspace)) || (reinterpret_cast<uintptr_t>(lens) & 3u) != 0)
+    return XATTN_ERR_ALIGN;
+  xattn::launch_decode(dtype, xattn::Dims{B, T, H, Hkv, hd}, q, k, v, lens, o, lse,
+                       static_cast<float*>(workspace), scale, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 const char* xattn_strerror(int status) {
   switch (status) {
     case XATTN_OK: return "success";

@@ -1,0 +1,436 @@
+// decode_attn.hip -- decode attention for gfx950: one new query per (sequence,
+// query head) against that sequence's cached keys and values.
+//
+// The operation is the last row of causal attention ("xtrain evolution
+// overview", post-training stage, milestone M2a: one query against the cached
+// K/V with an ordinary softmax, equal to the last row of full causal attention;
+// M2b: sequences decoded together each bring their own cache; M2c: the cache is
+// device-resident, one [T, hd] plane per (sequence, kv head)).  Query head h
+// reads kv head h / group as in row T15 of the same page's infra table.
+//
+// It is HBM-bound: every cached key and value is read once and the arithmetic
+// per byte is small (4 * group flops per 2 bytes of bf16 cache), so the design
+// goal is a streaming read of the cache with enough bytes in flight, not matrix
+// cores.  Work split ("split-K" over the cache):
+//   * a workgroup takes one kv head of one sequence, a chunk of C positions of
+//     its cache, and GC of the query heads that read that kv head (all of the
+//     group when it is at most 8), so each K/V byte is read once per GC heads;
+//   * lanes split a key row into 16-byte pieces (TPK lanes per key), so a wave
+//     reads KPW consecutive rows, one contiguous 1 KB (bf16 hd 64) block, per
+//     load instruction;
+//   * pass 1 computes the chunk's scores into LDS and their maximum, an exp
+//     pass turns them into weights and their sum, pass 2 accumulates the
+//     weighted values -- no rescaling of running sums is ever needed;
+//   * with more than one chunk per sequence each workgroup writes its partial
+//     (unnormalised sum, max, weight sum) and a second kernel merges the chunks
+//     in ascending order.  Fixed orders throughout: results are bitwise
+//     reproducible run to run.
+// Scores are kept in base-2 units (q is pre-multiplied by scale * log2 e).
+#include "attn_device.hpp"
+#include "launch.hpp"
+
+namespace xattn {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / kWave;
+constexpr int kDecMaxChunk = 1024;
+constexpr int kDecMinChunk = 256;
+// Most chunks per sequence the merge kernel takes (its LDS holds one weight per
+// chunk); longer caches use longer chunks.
+constexpr int kDecMaxChunkRecords = 4096;
+static_assert((long)kDecMaxChunk * kDecMaxChunkRecords == kDecodeMaxT, "decode limits");
+
+template <typename T, int HD>
+struct DecCfg {
+  static constexpr int EPL = 16 / (int)sizeof(T);  // elements per lane per load
+  static constexpr int TPK = HD / EPL;             // lanes per key row
+  static constexpr int KPW = kWave / TPK;          // keys per wave per round
+  static constexpr int KPR = kDecWaves * KPW;      // keys per workgroup per round
+  static_assert(TPK >= 1 && TPK <= kWave && kDecMaxChunk % KPR == 0, "decode tiling");
+};
+
+// 16 bytes of a row, kept raw while the load is in flight, widened to EPL
+// floats where they are used
+__device__ __forceinline__ uint4 load_raw(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+template <typename T>
+__device__ __forceinline__ void widen(const uint4& r, float* out);
+template <>
+__device__ __forceinline__ void widen<float>(const uint4& r, float* out) {
+  out[0] = __builtin_bit_cast(float, r.x); out[1] = __builtin_bit_cast(float, r.y);
+  out[2] = __builtin_bit_cast(float, r.z); out[3] = __builtin_bit_cast(float, r.w);
+}
+template <>
+__device__ __forceinline__ void widen<bf16>(const uint4& r, float* out) {
+  const bf16x8 v = __builtin_bit_cast(bf16x8, r);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
+}
+template <typename T>
+__device__ __forceinline__ void load_piece(const T* p, float* out) {
+  widen<T>(load_raw(p), out);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_one(T* p, float x);
+template <>
+__device__ __forceinline__ void store_one<float>(float* p, float x) { *p = x; }
+template <>
+__device__ __forceinline__ void store_one<bf16>(bf16* p, float x) { *p = (bf16)x; }
+
+// Partial record of one (sequence, query head, chunk) in the workspace:
+// HD unnormalised weighted-value sums, then the chunk's max score (base 2) and
+// its weight sum.
+template <int HD>
+struct Part {
+  static constexpr int STRIDE = HD + 2;
+};
+
+template <typename T, int HD, int GC>
+__global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const int* __restrict__ lens, T* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ part, int Tc, int H, int Hkv, int group, int nsplit, int chunk,
+    float scale_log2) {
+  using C = DecCfg<T, HD>;
+  constexpr int EPL = C::EPL, TPK = C::TPK, KPW = C::KPW, KPR = C::KPR;
+  // loads in flight per thread; a chunk's rounds (chunk / KPR, chunk a power of
+  // two >= kDecMinChunk) are a multiple of U
+  // (4 measured best: deeper pipelines cost registers, hence resident waves)
+  constexpr int U = 4 < kDecMinChunk / KPR ? 4 : kDecMinChunk / KPR;
+  __shared__ float sc[GC][kDecMaxChunk];
+  __shared__ float red[kDecWaves][GC][HD];
+  __shared__ float wred[kDecWaves][GC];
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int slot = lane / TPK, piece = lane % TPK;
+  const int split = blockIdx.x % nsplit;
+  const int unit = blockIdx.x / nsplit;  // (b * Hkv + g) * nhc + hc
+  const int nhc = group / GC;
+  const int hc = unit % nhc;
+  const int bg = unit / nhc;  // b * Hkv + g
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int h0 = g * group + hc * GC;
+
+  int n = lens ? lens[b] : Tc;
+  n = n < 0 ? 0 : (n > Tc ? Tc : n);
+  const int j0 = split * chunk;
+  const int j1 = min(j0 + chunk, n);
+
+  if (j0 >= j1) {  // nothing cached in this chunk
+    if (nsplit == 1) {
+      for (int i = tid; i < GC * HD; i += kDecThreads)
+        store_one<T>(o + (size_t)(b * H + h0 + i / HD) * HD + i % HD, 0.f);
+      if (tid < GC) lse[b * H + h0 + tid] = -__builtin_inff();
+    } else {
+      for (int i = tid; i < GC * (HD + 2); i += kDecThreads) {
+        const int t = i / (HD + 2), d = i % (HD + 2);
+        part[((size_t)(b * H + h0 + t) * nsplit + split) * Part<HD>::STRIDE + d] =
+            d == HD ? -__builtin_inff() : 0.f;
+      }
+    }
+    return;
+  }
+
+  float qv[GC][EPL];
+#pragma unroll
+  for (int t = 0; t < GC; ++t) {
+    load_piece<T>(q + (size_t)(b * H + h0 + t) * HD + piece * EPL, qv[t]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[t][e] *= scale_log2;
+  }
+
+  const size_t plane = ((size_t)b * Hkv + g) * (size_t)Tc * HD;
+  const T* kp = k + plane + piece * EPL;
+  const T* vp = v + plane + piece * EPL;
+  const int rounds = chunk / KPR;
+
+  // pass 1: scores of the chunk (base 2) into LDS, and this thread's maximum.
+  // Rolling pipeline: slot u holds the key piece of round r0 + u and is refilled
+  // with round r0 + u + U as soon as it is used, so U loads stay in flight.
+  // A round past the cached length loads the last cached row instead (always
+  // in bounds) and scores -inf.
+  auto row_of = [&](int r) __attribute__((always_inline)) {
+    const int j = j0 + r * KPR + wave * KPW + slot;
+    return (size_t)(j < j1 ? j : j1 - 1) * HD;
+  };
+  float mloc[GC];
+#pragma unroll
+  for (int t = 0; t < GC; ++t) mloc[t] = -__builtin_inff();
+  uint4 buf[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) buf[u] = load_raw(kp + row_of(u));
+  for (int r0 = 0; r0 < rounds; r0 += U) {  // rounds is a multiple of U
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u;
+      const int jj = r * KPR + wave * KPW + slot;  // position within the chunk
+      const bool live = j0 + jj < j1;
+      float kv[EPL];
+      widen<T>(buf[u], kv);
+      // refill (past the last round: the chunk's last row again, a cache hit)
+      buf[u] = load_raw(kp + row_of(r + U < rounds ? r + U : rounds - 1));
+      float sv[GC];
+#pragma unroll
+      for (int t = 0; t < GC; ++t) {
+        float acc1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc1 += qv[t][e] * kv[e];
+        sv[t] = acc1;
+      }
+#pragma unroll
+      for (int off = 1; off < TPK; off *= 2) {
+#pragma unroll
+        for (int t = 0; t < GC; ++t) sv[t] += __shfl_xor(sv[t], off);
+      }
+#pragma unroll
+      for (int t = 0; t < GC; ++t) {
+        const float st = live ? sv[t] : -__builtin_inff();
+        mloc[t] = fmaxf(mloc[t], st);
+        if (t % TPK == piece) sc[t][jj] = st;
+      }
+    }
+  }
+
+  // maximum of each head's scores over the workgroup
+#pragma unroll
+  for (int t = 0; t < GC; ++t) {
+#pragma unroll
+    for (int off = TPK; off < kWave; off *= 2) mloc[t] = fmaxf(mloc[t], __shfl_xor(mloc[t], off));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < GC; ++t) wred[wave][t] = mloc[t];
+  }
+  __syncthreads();
+  float M[GC];
+#pragma unroll
+  for (int t = 0; t < GC; ++t) {
+    M[t] = wred[0][t];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) M[t] = fmaxf(M[t], wred[w][t]);
+  }
+  __syncthreads();  // wred is reused for the weight sums
+
+  // first U rounds of values in flight while the weights are formed
+#pragma unroll
+  for (int u = 0; u < U; ++u) buf[u] = load_raw(vp + row_of(u));
+
+  // weights exp2(s - M) in place, and each head's weight sum
+  float lsum[GC];
+#pragma unroll
+  for (int t = 0; t < GC; ++t) {
+    float a = 0.f;
+    for (int jj = tid; jj < chunk; jj += kDecThreads) {
+      const float p = fast_exp2(sc[t][jj] - M[t]);
+      sc[t][jj] = p;
+      a += p;
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off *= 2) a += __shfl_xor(a, off);
+    lsum[t] = a;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < GC; ++t) wred[wave][t] = lsum[t];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < GC; ++t) {
+    lsum[t] = wred[0][t];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) lsum[t] += wred[w][t];
+  }
+
+  // pass 2: weighted values, the same rolling pipeline over V (a round past the
+  // cached length has weight 0 and its piece is zeroed)
+  float acc[GC][EPL];
+#pragma unroll
+  for (int t = 0; t < GC; ++t)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
+  for (int r0 = 0; r0 < rounds; r0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u;
+      const int jj = r * KPR + wave * KPW + slot;
+      const bool live = j0 + jj < j1;
+      float vv[EPL];
+      widen<T>(buf[u], vv);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) vv[e] = live ? vv[e] : 0.f;
+      buf[u] = load_raw(vp + row_of(r + U < rounds ? r + U : rounds - 1));
+#pragma unroll
+      for (int t = 0; t < GC; ++t) {
+        const float p = sc[t][jj];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[t][e] += p * vv[e];
+      }
+    }
+  }
+
+  // sum over the key slots of a wave (lanes of equal piece), then over waves
+#pragma unroll
+  for (int off = TPK; off < kWave; off *= 2) {
+#pragma unroll
+    for (int t = 0; t < GC; ++t)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[t][e] += __shfl_xor(acc[t][e], off);
+  }
+  if (slot == 0) {
+#pragma unroll
+    for (int t = 0; t < GC; ++t)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red[wave][t][piece * EPL + e] = acc[t][e];
+  }
+  __syncthreads();
+  for (int i = tid; i < GC * HD; i += kDecThreads) {
+    const int t = i / HD, d = i % HD;
+    float a = red[0][t][d];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) a += red[w][t][d];
+    const int h = h0 + t;
+    float mt = M[0], lt = lsum[0];
+#pragma unroll
+    for (int u = 1; u < GC; ++u)
+      if (t == u) { mt = M[u]; lt = lsum[u]; }
+    if (nsplit == 1) {
+      store_one<T>(o + (size_t)(b * H + h) * HD + d, a / lt);
+      if (d == 0) lse[b * H + h] = (mt + fast_log2(lt)) * kLn2;
+    } else {
+      float* pr = part + ((size_t)(b * H + h) * nsplit + split) * Part<HD>::STRIDE;
+      pr[d] = a;
+      if (d == 0) {
+        pr[HD] = mt;
+        pr[HD + 1] = lt;
+      }
+    }
+  }
+}
+
+// Merge the chunks of each (sequence, query head): one workgroup per row.
+// Thread c < nsplit brings chunk c's max and weight sum; the row max and the
+// merged weight sum are formed in a fixed pairwise order in LDS.  For the
+// weighted sums, thread t takes element d = t % HD of the chunks c = t / HD,
+// t / HD + NG, ... (NG = 256 / HD groups, independent loads in flight), and the
+// NG group sums are added in ascending group order.
+template <typename T, int HD>
+__global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(
+    const float* __restrict__ part, T* __restrict__ o, float* __restrict__ lse, int nsplit) {
+  constexpr int NG = kDecThreads / HD;
+  __shared__ float red[kDecThreads];
+  __shared__ float wsc[kDecMaxChunkRecords];
+  __shared__ float acc_g[NG][HD];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const float* pr = part + (size_t)row * nsplit * Part<HD>::STRIDE;
+
+  // row max over the chunks (strided per thread, then a fixed tree)
+  float m = -__builtin_inff();
+  for (int c = t; c < nsplit; c += kDecThreads) m = fmaxf(m, pr[(size_t)c * Part<HD>::STRIDE + HD]);
+  red[t] = m;
+  __syncthreads();
+  for (int n = kDecThreads / 2; n >= 1; n /= 2) {
+    if (t < n) red[t] = fmaxf(red[t], red[t + n]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  if (M == -__builtin_inff()) {  // empty sequence
+    if (t < HD) store_one<T>(o + (size_t)row * HD + t, 0.f);
+    if (t == 0) lse[row] = -__builtin_inff();
+    return;
+  }
+  // chunk weights (0 for an empty chunk, whose max is -inf) and the merged weight sum
+  float l = 0.f;
+  for (int c = t; c < nsplit; c += kDecThreads) {
+    const float w = fast_exp2(pr[(size_t)c * Part<HD>::STRIDE + HD] - M);
+    wsc[c] = w;
+    l += w * pr[(size_t)c * Part<HD>::STRIDE + HD + 1];
+  }
+  red[t] = l;
+  __syncthreads();
+  for (int n = kDecThreads / 2; n >= 1; n /= 2) {
+    if (t < n) red[t] += red[t + n];
+    __syncthreads();
+  }
+  const float L = red[0];
+
+  const int d = t % HD, g0 = t / HD;
+  float a = 0.f;
+#pragma unroll 8
+  for (int c = g0; c < nsplit; c += NG) a += wsc[c] * pr[(size_t)c * Part<HD>::STRIDE + d];
+  acc_g[g0][d] = a;
+  __syncthreads();
+  if (t < HD) {
+    float s = acc_g[0][t];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) s += acc_g[g][t];
+    store_one<T>(o + (size_t)row * HD + t, s / L);
+    if (t == 0) lse[row] = (M + fast_log2(L)) * kLn2;
+  }
+}
+
+static int heads_per_wg(int group) {
+  for (int gc = 8; gc > 1; gc /= 2)
+    if (group % gc == 0) return gc;
+  return 1;
+}
+
+DecodePlan decode_plan(int B, int T, int H, int Hkv, int hd) {
+  const int group = H / Hkv;
+  const long units = (long)B * Hkv * (group / heads_per_wg(group));
+  int chunk = kDecMinChunk;
+  // about four workgroups per CU (one resident wave of them), chunks as short as that allows
+  while (chunk < kDecMaxChunk && units * ((T + chunk - 1) / chunk) > 1024) chunk *= 2;
+  DecodePlan p;
+  p.chunk = chunk;
+  p.nsplit = (T + chunk - 1) / chunk;
+  p.blocks = p.nsplit * units;
+  p.part_bytes = p.nsplit > 1 ? sizeof(float) * (size_t)B * H * p.nsplit * (hd + 2) : 0;
+  return p;
+}
+
+template <typename T, int HD, int GC>
+static void decode_launch(const Dims& d, const DecodePlan& p, const void* q, const void* k,
+                          const void* v, const int* lens, void* o, float* lse, float* part,
+                          float scale, hipStream_t stream) {
+  const int group = d.H / d.Hkv;
+  const dim3 grid((unsigned)((long)p.nsplit * d.B * d.Hkv * (group / GC)));
+  hipLaunchKernelGGL((decode_attn_kernel<T, HD, GC>), grid, dim3(kDecThreads), 0, stream,
+                     (const T*)q, (const T*)k, (const T*)v, lens, (T*)o, lse, part, d.S, d.H,
+                     d.Hkv, group, p.nsplit, p.chunk, scale * kLog2e);
+  if (p.nsplit > 1) {
+    hipLaunchKernelGGL((decode_combine_kernel<T, HD>), dim3((unsigned)(d.B * d.H)),
+                       dim3(kDecThreads), 0, stream, part, (T*)o, lse, p.nsplit);
+  }
+}
+
+template <typename T, int HD>
+static void decode_hd(const Dims& d, const DecodePlan& p, const void* q, const void* k,
+                      const void* v, const int* lens, void* o, float* lse, float* part,
+                      float scale, hipStream_t stream) {
+  switch (heads_per_wg(d.H / d.Hkv)) {
+    case 8: decode_launch<T, HD, 8>(d, p, q, k, v, lens, o, lse, part, scale, stream); break;
+    case 4: decode_launch<T, HD, 4>(d, p, q, k, v, lens, o, lse, part, scale, stream); break;
+    case 2: decode_launch<T, HD, 2>(d, p, q, k, v, lens, o, lse, part, scale, stream); break;
+    default: decode_launch<T, HD, 1>(d, p, q, k, v, lens, o, lse, part, scale, stream); break;
+  }
+}
+
+void launch_decode(int dtype, const Dims& d, const void* q, const void* k, const void* v,
+                   const int* lens, void* o, float* lse, float* part, float scale,
+                   hipStream_t stream) {
+  const DecodePlan p = decode_plan(d.B, d.S, d.H, d.Hkv, d.hd);
+  if (dtype == 0) {
+    if (d.hd == 16) decode_hd<float, 16>(d, p, q, k, v, lens, o, lse, part, scale, stream);
+    else if (d.hd == 32) decode_hd<float, 32>(d, p, q, k, v, lens, o, lse, part, scale, stream);
+    else decode_hd<float, 64>(d, p, q, k, v, lens, o, lse, part, scale, stream);
+  } else {
+    if (d.hd == 16) decode_hd<bf16, 16>(d, p, q, k, v, lens, o, lse, part, scale, stream);
+    else if (d.hd == 32) decode_hd<bf16, 32>(d, p, q, k, v, lens, o, lse, part, scale, stream);
+    else decode_hd<bf16, 64>(d, p, q, k, v, lens, o, lse, part, scale, stream);
+  }
+}
+
+}  // namespace xattn

@@ -43,4 +43,21 @@ void launch_qknorm_rope_bwd(int dtype, const NormDims& d, const void* x, const f
                             const float* dout, float* dx, float* dw, float* ws, float eps,
                             float base, hipStream_t stream);
 
+// Decode attention: q, o [B][H][hd]; k, v [B][Hkv][T][hd] with T in Dims::S;
+// lens [B] (nullable); part is the workspace (nullable when part_bytes == 0).
+struct DecodePlan {
+  int chunk;          // cache positions per workgroup
+  int nsplit;         // chunks per sequence
+  long blocks;        // workgroups of the main kernel
+  size_t part_bytes;  // workspace: partial records when nsplit > 1
+};
+DecodePlan decode_plan(int B, int T, int H, int Hkv, int hd);
+
+// Longest cache decode accepts: 4096 chunks of at most 1024 positions.
+constexpr long kDecodeMaxT = 4096L * 1024;
+
+void launch_decode(int dtype, const Dims& d, const void* q, const void* k, const void* v,
+                   const int* lens, void* o, float* lse, float* part, float scale,
+                   hipStream_t stream);
+
 }  // namespace xattn

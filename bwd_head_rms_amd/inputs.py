@@ -89,9 +89,14 @@ def rope(x, base=10000.0):
 def bf16_bits(x):
     """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounding = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + rounding) >> 16).astype(np.uint16)
+    if x.size >= 1 << 22:  # large draws: torch's multithreaded conversion, also RNE
+        import torch
+        out = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        out = out.copy()
+    else:
+        u = x.view(np.uint32)
+        # u + 0x7FFF + lsb stays below 2^32 for every non-NaN pattern (NaNs are set below)
+        out = ((u + (((u >> 16) & 1) + np.uint32(0x7FFF))) >> 16).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = 0x7FC0
@@ -100,7 +105,10 @@ def bf16_bits(x):
 
 def bf16_round(x):
     """float32 values rounded to the nearest bfloat16 (returned as float32)."""
-    return (bf16_bits(x).astype(np.uint32) << 16).view(np.float32)
+    b = bf16_bits(x)
+    out = np.empty(b.shape, dtype=np.uint32)
+    np.left_shift(b, 16, out=out, dtype=np.uint32)
+    return out.view(np.float32)
 
 
 def generate(B, S, H, Hkv, hd, seed, shaped=True, dtype="f32"):
@@ -129,6 +137,80 @@ def generate_workload(w):
     if isinstance(w, str):
         w = WORKLOADS[w]
     return generate(w.B, w.S, w.H, w.Hkv, w.hd, w.seed, w.shaped, w.dtype)
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decode step: a new query per (sequence, head) against a K/V cache of T
+    positions.  ``source`` names the attention workload whose last query row
+    and full K/V it reuses (decode equals the last row of causal attention
+    there); without a source, q, k, v are drawn i.i.d. N(0, 1) (a cache too big
+    for the shaping pass to be worth its time; the scores have the same spread,
+    |s| ~ N(0, 1) with scale 1/sqrt(hd))."""
+    name: str
+    B: int
+    T: int
+    H: int
+    Hkv: int
+    hd: int
+    dtype: str
+    seed: int
+    source: str = None
+
+    @property
+    def scale(self):
+        return 1.0 / float(np.sqrt(self.hd))
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        DecodeWorkload("decode_long_b4_t2048_h16_hd64_bf16", 4, 2048, 16, 16, 64, "bf16", 5,
+                       "long_b4_s2048_h16_hd64_bf16"),
+        DecodeWorkload("decode_gqa_b16_t1024_h8_kv2_hd64_bf16", 16, 1024, 8, 2, 64, "bf16", 4,
+                       "gqa_b16_s1024_h8_kv2_hd64_bf16"),
+        DecodeWorkload("decode_gqa_b16_t1024_h8_kv2_hd64_f32", 16, 1024, 8, 2, 64, "f32", 4,
+                       "gqa_b16_s1024_h8_kv2_hd64_f32"),
+        DecodeWorkload("decode_cache_b8_t32768_h16_kv4_hd64_bf16", 8, 32768, 16, 4, 64, "bf16", 6),
+    ]
+}
+
+# The decode workload the benchmark times against the HBM roofline.
+DECODE_BENCH = "decode_cache_b8_t32768_h16_kv4_hd64_bf16"
+
+
+def _normal_blocks(shape, seed_seq, blocks=16):
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    edges = np.linspace(0, flat.size, blocks + 1).astype(np.int64)
+    gens = [np.random.default_rng(s) for s in seed_seq.spawn(blocks)]
+
+    def fill(i):
+        gens[i].standard_normal(dtype=np.float32, out=flat[edges[i]:edges[i + 1]])
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(fill, range(blocks)))
+    return out
+
+
+def generate_decode(w):
+    """q [B,H,hd], k, v [B,Hkv,T,hd] float32 (bf16-rounded for bf16 workloads)."""
+    if isinstance(w, str):
+        w = DECODE_WORKLOADS[w]
+    if w.source:
+        a = generate_workload(w.source)
+        return {"q": np.ascontiguousarray(a["q"][:, :, w.T - 1]), "k": a["k"], "v": a["v"]}
+    # q, k, v from three child streams of the seed; each cache tensor is filled
+    # in 16 fixed blocks by 16 further child streams, in threads (the result does
+    # not depend on how many threads run)
+    sq, sk, sv = np.random.SeedSequence(w.seed).spawn(3)
+    out = {"q": np.random.default_rng(sq).standard_normal((w.B, w.H, w.hd), dtype=np.float32),
+           "k": _normal_blocks((w.B, w.Hkv, w.T, w.hd), sk),
+           "v": _normal_blocks((w.B, w.Hkv, w.T, w.hd), sv)}
+    if w.dtype == "bf16":
+        out = {n: bf16_round(a) for n, a in out.items()}
+    return out
 
 
 def to_torch(a, dtype, device):

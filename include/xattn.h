@@ -184,6 +184,42 @@ int xattn_qknorm_rope_bwd(const void* x, const float* w, const float* dout, floa
                           int B, int S, int H, int hd, float eps, float rope_base, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode attention: the new query of each sequence against that sequence's
+ * key/value cache (the decode-attention primitive of the "xtrain evolution
+ * overview" page, post-training stage: milestone M2a -- one query against the
+ * cached K/V, equal to the last row of full causal attention; M2b -- several
+ * sequences decoded together, each with its own cache, GQA broadcasting each kv
+ * head to its group; M2c -- the cache kept on the device, one [T, hd] plane per
+ * (sequence, kv head)).  For sequence b holding n = lens[b] positions, query
+ * head h, kv head g = h / (H / Hkv):
+ *
+ *   s_j = scale * q[b,h] . k[b,g,j]   (j < n),   lse[b,h] = ln sum_{j<n} exp(s_j),
+ *   o[b,h] = sum_{j<n} exp(s_j - lse[b,h]) v[b,g,j]
+ *
+ * and for n = 0: o[b,h] = 0, lse[b,h] = -inf.  Positions j >= n are never read.
+ *
+ *   q, o    [B][H][hd]        in `dtype` (o overwritten; rounded to nearest-even in bf16)
+ *   k, v    [B][Hkv][T][hd]   in `dtype`, T = cache capacity, at most 4194304 (inputs)
+ *   lens    [B] int32 device array, or NULL (every sequence holds T positions).
+ *           Values are clamped to [0, T] on the device (they cannot be checked on
+ *           the host without a synchronisation).
+ *   lse     [B][H] float, natural log, scale included (output)
+ *   workspace: device scratch of at least xattn_decode_workspace_bytes bytes,
+ *           16-byte aligned, contents on entry irrelevant; may be NULL when that
+ *           size is 0.
+ * Arithmetic is fp32 (bf16 inputs are widened exactly).  Long caches are split
+ * into chunks handled by separate workgroups, merged by a second kernel in a
+ * fixed order: bitwise reproducible run to run.  Same pointer, stream and error
+ * rules as xattn_fwd (data pointers 16-byte aligned; lens 4-byte aligned).
+ * Returns an xattn_status.
+ */
+size_t xattn_decode_workspace_bytes(int B, int T, int H, int Hkv, int hd);
+
+int xattn_decode(const void* q, const void* k, const void* v, const int* lens, void* o,
+                 float* lse, int B, int T, int H, int Hkv, int hd, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 const char* xattn_strerror(int status);
 
 #ifdef __cplusplus

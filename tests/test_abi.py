@@ -201,3 +201,44 @@ def test_norm_workspace_bytes(L):
     assert f(4, 2048, 16, 64) == 4 * 64 * 1024               # capped grid
     assert f(0, 4, 2, 16) == 0 and f(1, 4, 2, 48) == 0
     assert L.xattn_strerror(PARAM).decode().startswith("eps")
+
+
+# -- decode attention ------------------------------------------------------------
+def dec(L, ws=P, ws_bytes=None, B=4, T=2048, H=16, Hkv=16, hd=64, scale=0.125, dtype=1, lens=P,
+        **ptrs):
+    p = {n: P for n in ("q", "k", "v", "o", "lse")}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = L.xattn_decode_workspace_bytes(B, T, H, Hkv, hd)
+    return L.xattn_decode(p["q"], p["k"], p["v"], lens, p["o"], p["lse"], B, T, H, Hkv, hd, scale,
+                          dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_decode_null_pointer(L, name):
+    assert dec(L, **{name: None}) == NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), SHAPE), (dict(T=0), SHAPE), (dict(H=0), SHAPE), (dict(Hkv=-2), SHAPE),
+    (dict(H=6, Hkv=4), GQA), (dict(hd=8), HEAD_DIM), (dict(hd=128), HEAD_DIM),
+    (dict(dtype=3), DTYPE), (dict(scale=0.0), SCALE), (dict(scale=float("nan")), SCALE),
+    (dict(T=1 << 26, hd=64), SHAPE), (dict(T=(1 << 22) + 1, hd=16), SHAPE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1024), WORKSPACE),
+    (dict(q=P + 8), ALIGN), (dict(k=P + 4), ALIGN), (dict(o=P + 2), ALIGN), (dict(ws=P + 8), ALIGN),
+    (dict(lens=P + 2), ALIGN)])
+def test_decode_rejects(L, kw, status):
+    assert dec(L, **kw) == status
+
+
+def test_decode_workspace_bytes(L):
+    f = L.xattn_decode_workspace_bytes
+    # one chunk per sequence needs no workspace: at least 256 positions per workgroup
+    assert f(1, 100, 2, 2, 16) == 0 and f(1, 256, 2, 2, 16) == 0
+    # 64 (sequence, kv head) units x 8 chunks of 256: one record of hd + 2 floats each
+    assert f(4, 2048, 16, 16, 64) == 4 * 4 * 16 * 8 * 66
+    # a long cache: chunks grow to 1024 positions (64 units x 32 chunks)
+    assert f(4, 32768, 16, 16, 64) == 4 * 4 * 16 * 32 * 66
+    # 8 x 4 units x 32 chunks of 1024 (group 4: one workgroup takes all 4 query heads)
+    assert f(8, 32768, 16, 4, 64) == 4 * 8 * 16 * 32 * 66
+    assert f(0, 16, 2, 2, 16) == 0 and f(1, 16, 3, 2, 16) == 0 and f(1, 16, 2, 2, 48) == 0
