@@ -310,32 +310,47 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
 }
 
 // Merge the chunks of each (sequence, query head): one workgroup per row.
-// Thread c < nsplit brings chunk c's max and weight sum; the row max and the
-// merged weight sum are formed in a fixed pairwise order in LDS.  For the
-// weighted sums, thread t takes element d = t % HD of the chunks c = t / HD,
-// t / HD + NG, ... (NG = 256 / HD groups, independent loads in flight), and the
-// NG group sums are added in ascending group order.
+// Every load is issued up front (the weighted sums do not depend on the row
+// max): thread c brings chunk c's max and weight sum, thread t the element
+// d = t % HD of chunks t / HD, t / HD + NG, ... (NG = 256 / HD groups).  The
+// row max and the merged weight sum are reduced in a fixed order (within each
+// wave, then across the 4 waves in ascending order), the NG group sums of each
+// element in ascending group order.
 template <typename T, int HD>
 __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(
     const float* __restrict__ part, T* __restrict__ o, float* __restrict__ lse, int nsplit) {
   constexpr int NG = kDecThreads / HD;
-  __shared__ float red[kDecThreads];
+  constexpr int CR = 8;  // chunk records per thread held in registers
+  constexpr int STRIDE = Part<HD>::STRIDE;
+  __shared__ float wmax[kDecWaves], wsum[kDecWaves];
   __shared__ float wsc[kDecMaxChunkRecords];
   __shared__ float acc_g[NG][HD];
-  const int row = blockIdx.x, t = threadIdx.x;
-  const float* pr = part + (size_t)row * nsplit * Part<HD>::STRIDE;
+  const int row = blockIdx.x, t = threadIdx.x, wave = t / kWave;
+  const int d = t % HD, g0 = t / HD;
+  const float* pr = part + (size_t)row * nsplit * STRIDE;
 
-  // row max over the chunks (strided per thread, then a fixed tree)
-  float m = -__builtin_inff();
-  for (int c = t; c < nsplit; c += kDecThreads) m = fmaxf(m, pr[(size_t)c * Part<HD>::STRIDE + HD]);
-  red[t] = m;
-  __syncthreads();
-  for (int n = kDecThreads / 2; n >= 1; n /= 2) {
-    if (t < n) red[t] = fmaxf(red[t], red[t + n]);
-    __syncthreads();
+  float pre[CR];
+#pragma unroll
+  for (int i = 0; i < CR; ++i) {
+    const int c = g0 + NG * i;
+    pre[i] = c < nsplit ? pr[(size_t)c * STRIDE + d] : 0.f;
   }
-  const float M = red[0];
+  float m0 = -__builtin_inff(), l0 = 0.f;  // chunk t's record
+  if (t < nsplit) {
+    m0 = pr[(size_t)t * STRIDE + HD];
+    l0 = pr[(size_t)t * STRIDE + HD + 1];
+  }
+  float m = m0;
+  for (int c = t + kDecThreads; c < nsplit; c += kDecThreads)
+    m = fmaxf(m, pr[(size_t)c * STRIDE + HD]);
+
+#pragma unroll
+  for (int off = 1; off < kWave; off *= 2) m = fmaxf(m, __shfl_xor(m, off));
+  if (t % kWave == 0) wmax[wave] = m;
   __syncthreads();
+  float M = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, wmax[w]);
   if (M == -__builtin_inff()) {  // empty sequence
     if (t < HD) store_one<T>(o + (size_t)row * HD + t, 0.f);
     if (t == 0) lse[row] = -__builtin_inff();
@@ -343,30 +358,38 @@ __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(
   }
   // chunk weights (0 for an empty chunk, whose max is -inf) and the merged weight sum
   float l = 0.f;
-  for (int c = t; c < nsplit; c += kDecThreads) {
-    const float w = fast_exp2(pr[(size_t)c * Part<HD>::STRIDE + HD] - M);
+  if (t < nsplit) {
+    const float w = fast_exp2(m0 - M);
+    wsc[t] = w;
+    l = w * l0;
+  }
+  for (int c = t + kDecThreads; c < nsplit; c += kDecThreads) {
+    const float w = fast_exp2(pr[(size_t)c * STRIDE + HD] - M);
     wsc[c] = w;
-    l += w * pr[(size_t)c * Part<HD>::STRIDE + HD + 1];
+    l += w * pr[(size_t)c * STRIDE + HD + 1];
   }
-  red[t] = l;
+#pragma unroll
+  for (int off = 1; off < kWave; off *= 2) l += __shfl_xor(l, off);
+  if (t % kWave == 0) wsum[wave] = l;
   __syncthreads();
-  for (int n = kDecThreads / 2; n >= 1; n /= 2) {
-    if (t < n) red[t] += red[t + n];
-    __syncthreads();
-  }
-  const float L = red[0];
+  float L = wsum[0];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) L += wsum[w];
 
-  const int d = t % HD, g0 = t / HD;
   float a = 0.f;
-#pragma unroll 8
-  for (int c = g0; c < nsplit; c += NG) a += wsc[c] * pr[(size_t)c * Part<HD>::STRIDE + d];
+#pragma unroll
+  for (int i = 0; i < CR; ++i) {
+    const int c = g0 + NG * i;
+    if (c < nsplit) a += wsc[c] * pre[i];
+  }
+  for (int c = g0 + NG * CR; c < nsplit; c += NG) a += wsc[c] * pr[(size_t)c * STRIDE + d];
   acc_g[g0][d] = a;
   __syncthreads();
   if (t < HD) {
-    float s = acc_g[0][t];
+    float sum = acc_g[0][t];
 #pragma unroll
-    for (int g = 1; g < NG; ++g) s += acc_g[g][t];
-    store_one<T>(o + (size_t)row * HD + t, s / L);
+    for (int g = 1; g < NG; ++g) sum += acc_g[g][t];
+    store_one<T>(o + (size_t)row * HD + t, sum / L);
     if (t == 0) lse[row] = (M + fast_log2(L)) * kLn2;
   }
 }
