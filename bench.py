@@ -23,8 +23,10 @@ MI355X's HBM bandwidth (algorithmic bytes: fwd reads x and writes out; bwd
 reads x and the fp32 upstream gradient and writes the fp32 dx), and decode
 attention (one new query per sequence and head against a K/V cache) on a
 32768-position bf16 cache and on the long-context workload's last row, against
-the same bandwidth (algorithmic bytes: the cached K and V once, q, o and lse).
-Neither is part of the timed attention step.
+the same bandwidth (algorithmic bytes: the cached K and V once, q, o and lse),
+and a right-padded batch of 8 sequences with lengths 256..2048 through the
+length-aware kernels, against the same batch run padded.  None of them is part
+of the timed attention step.
 
 Prints ONE JSON line.
 """
@@ -301,6 +303,69 @@ def run_decode(wd, steps, warmup):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBPS, 4), "alg_bytes": nb}}
 
 
+def run_ragged(rw, steps, warmup):
+    """Time fwd + bwd of a right-padded batch with its lengths (xattn_fwd_ragged,
+    xattn_bwd_ragged) and, for comparison, the plain kernels over the same
+    padded batch.  TFLOP/s counts the causal work of the real rows only."""
+    import numpy as np
+    import torch
+
+    from bwd_head_rms_amd import _lib, inputs
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    lens = rw.lens()
+    a = inputs.generate(rw.B, rw.S, rw.H, rw.Hkv, rw.hd, rw.seed, shaped=True, dtype=rw.dtype)
+    t = {n: inputs.to_torch(x, rw.dtype, dev) for n, x in a.items()}
+    del a
+    tl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((rw.B, rw.H, rw.S), dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty(t["q"].shape, **f32)
+    dk = torch.empty(t["k"].shape, **f32)
+    dv = torch.empty(t["k"].shape, **f32)
+    code = _lib.BF16 if rw.dtype == "bf16" else _lib.F32
+    wsb = int(L.xattn_bwd_workspace_bytes(rw.B, rw.S, rw.H, rw.Hkv, rw.hd, code))
+    ws = torch.empty((wsb // 4,), **f32)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    dims = (rw.B, rw.S, rw.H, rw.Hkv, rw.hd, rw.scale, code)
+    p = {n: x.data_ptr() for n, x in dict(q=t["q"], k=t["k"], v=t["v"], dO=t["dO"], o=o, lse=lse,
+                                          dq=dq, dk=dk, dv=dv, ws=ws, lens=tl).items()}
+
+    def ragged():
+        _lib.check(L.xattn_fwd_ragged(p["q"], p["k"], p["v"], p["lens"], p["o"], p["lse"], *dims,
+                                      sh))
+        _lib.check(L.xattn_bwd_ragged(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["lens"],
+                                      p["dq"], p["dk"], p["dv"], *dims, p["ws"], wsb, sh))
+
+    def padded():
+        _lib.check(L.xattn_fwd(p["q"], p["k"], p["v"], p["o"], p["lse"], *dims, sh))
+        _lib.check(L.xattn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"],
+                               p["dk"], p["dv"], *dims, p["ws"], wsb, sh))
+
+    ms = {}
+    for name, fn in (("ragged", ragged), ("padded", padded)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / steps
+    flops = sum(14.0 * rw.hd * rw.H * n * (n + 1) / 2 for n in lens)
+    tf = flops / (ms["ragged"] / 1e3) / 1e12
+    return {"workload": rw.name, "lens": lens, "ms_per_step": round(ms["ragged"], 5),
+            "padded_ms_per_step": round(ms["padded"], 5),
+            "speedup_vs_padded": round(ms["padded"] / ms["ragged"], 3),
+            "tflops_real_rows": round(tf, 3),
+            "pct_of_mfma_peak": round(100 * tf / PEAK_TFLOPS[rw.dtype], 3),
+            "tokens_per_s": round(sum(lens) / (ms["ragged"] / 1e3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,7 +375,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the QK-norm + RoPE step and decode attention ('next_rows')")
+                    help="skip QK-norm + RoPE, decode and ragged batches ('next_rows')")
     ap.add_argument("--norm-only", action="store_true",
                     help="only time the QK-norm + RoPE step (for profiling its kernels)")
     ap.add_argument("--decode-only", action="store_true",
@@ -389,7 +454,8 @@ def main():
                                  args.warmup),
             "decode_long_context_last_row": run_decode(
                 inputs.DECODE_WORKLOADS["decode_long_b4_t2048_h16_hd64_bf16"], args.steps,
-                args.warmup)}
+                args.warmup),
+            "ragged": run_ragged(inputs.RAGGED_BENCH, args.steps, args.warmup)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)

@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so
 SYMBOLS = ("xattn_fwd", "xattn_bwd", "xattn_bwd_workspace_bytes", "xattn_bwd_dq",
            "xattn_bwd_dkdv", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
            "xattn_qknorm_rope_bwd", "xattn_decode_workspace_bytes", "xattn_decode",
+           "xattn_fwd_ragged", "xattn_bwd_ragged",
            "xattn_strerror")
 
 F32, BF16 = 0, 1
@@ -55,6 +56,10 @@ def lib():
     L.xattn_qknorm_rope_bwd_workspace_bytes.restype = sz
     L.xattn_qknorm_rope_bwd.argtypes = [vp] * 5 + [i, i, i, i, f, f, i, vp, sz, vp]
     L.xattn_qknorm_rope_bwd.restype = i
+    L.xattn_fwd_ragged.argtypes = [vp] * 6 + [i, i, i, i, i, f, i, vp]
+    L.xattn_fwd_ragged.restype = i
+    L.xattn_bwd_ragged.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp, sz, vp]
+    L.xattn_bwd_ragged.restype = i
     L.xattn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.xattn_decode_workspace_bytes.restype = sz
     L.xattn_decode.argtypes = [vp] * 6 + [i, i, i, i, i, f, i, vp, sz, vp]

@@ -42,12 +42,20 @@ def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def fwd(q, k, v, scale=None, o=None, lse=None):
+def _check_lens(lens, B):
+    if lens is not None:
+        _check_tensor(lens, "lens", (B,), torch.int32)
+
+
+def fwd(q, k, v, scale=None, o=None, lse=None, lens=None):
     """Causal attention forward.  q [B,H,S,hd]; k, v [B,Hkv,S,hd] (fp32 or bf16).
+    ``lens`` ([B] int32 on the device): right-padded batch, sequence b holds
+    lens[b] rows; padding rows come back as o = 0, lse = -inf.
 
     Returns (o [B,H,S,hd] in the input dtype, lse [B,H,S] fp32).
     """
     B, S, H, Hkv, hd = _dims(q, k)
+    _check_lens(lens, B)
     scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
     _check_tensor(q, "q", (B, H, S, hd), q.dtype)
     _check_tensor(k, "k", (B, Hkv, S, hd), q.dtype)
@@ -56,8 +64,13 @@ def fwd(q, k, v, scale=None, o=None, lse=None):
     lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor(o, "o", (B, H, S, hd), q.dtype)
     _check_tensor(lse, "lse", (B, H, S), torch.float32)
-    check(lib().xattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                          B, S, H, Hkv, hd, scale, _code(q), _stream(q)))
+    if lens is None:
+        check(lib().xattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, S, H, Hkv, hd, scale, _code(q), _stream(q)))
+    else:
+        check(lib().xattn_fwd_ragged(q.data_ptr(), k.data_ptr(), v.data_ptr(), lens.data_ptr(),
+                                     o.data_ptr(), lse.data_ptr(), B, S, H, Hkv, hd, scale,
+                                     _code(q), _stream(q)))
     return o, lse
 
 
@@ -65,9 +78,11 @@ def workspace_bytes(B, S, H, Hkv, hd, dtype_code):
     return int(lib().xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype_code))
 
 
-def bwd(q, k, v, o, lse, dO, scale=None, dq=None, dk=None, dv=None, workspace=None):
-    """Causal attention backward.  Returns fp32 (dq [B,H,S,hd], dk, dv [B,Hkv,S,hd])."""
+def bwd(q, k, v, o, lse, dO, scale=None, dq=None, dk=None, dv=None, workspace=None, lens=None):
+    """Causal attention backward.  Returns fp32 (dq [B,H,S,hd], dk, dv [B,Hkv,S,hd]).
+    ``lens`` as in ``fwd``: padding rows and keys get zero gradients."""
     B, S, H, Hkv, hd = _dims(q, k)
+    _check_lens(lens, B)
     scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
     dt = q.dtype
     for t, n, shp in ((q, "q", (B, H, S, hd)), (k, "k", (B, Hkv, S, hd)), (v, "v", (B, Hkv, S, hd)),
@@ -84,11 +99,17 @@ def bwd(q, k, v, o, lse, dO, scale=None, dq=None, dk=None, dv=None, workspace=No
     need = workspace_bytes(B, S, H, Hkv, hd, _code(q))
     if workspace is None:
         workspace = torch.empty((max(1, need // 4),), **f32)
-    check(lib().xattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                          dO.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                          B, S, H, Hkv, hd, scale, _code(q),
-                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                          _stream(q)))
+    wbytes = workspace.numel() * workspace.element_size()
+    if lens is None:
+        check(lib().xattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), dO.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), B, S, H, Hkv, hd, scale, _code(q),
+                              workspace.data_ptr(), wbytes, _stream(q)))
+    else:
+        check(lib().xattn_bwd_ragged(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     lse.data_ptr(), dO.data_ptr(), lens.data_ptr(), dq.data_ptr(),
+                                     dk.data_ptr(), dv.data_ptr(), B, S, H, Hkv, hd, scale,
+                                     _code(q), workspace.data_ptr(), wbytes, _stream(q)))
     return dq, dk, dv
 
 

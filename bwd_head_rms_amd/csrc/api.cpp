@@ -45,18 +45,80 @@ int launch_status() {
 
 }  // namespace
 
+namespace {
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int fwd_impl(const void* q, const void* k, const void* v, const int* lens, void* o, float* lse,
+             int B, int S, int H, int Hkv, int hd, float scale, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return XATTN_ERR_NULL;
+  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned4(lens))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_fwd(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, o, lse, lens, scale,
+                    static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int check_bwd_common(int B, int S, int H, int Hkv, int hd, float scale, int dtype,
+                     const void* workspace, size_t workspace_bytes);
+
+int bwd_dq_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, const int* lens, float* dq, int B, int S, int H, int Hkv, int hd,
+                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq) return XATTN_ERR_NULL;
+  const int rc = check_bwd_common(B, S, H, Hkv, hd, scale, dtype, workspace, workspace_bytes);
+  if (rc != XATTN_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dq) || !aligned16(workspace) || !aligned4(lens))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_bwd_dq(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, o, lse, dO, dq,
+                       static_cast<float*>(workspace), lens, scale,
+                       static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int bwd_dkdv_impl(const void* q, const void* k, const void* v, const float* lse, const void* dO,
+                  const int* lens, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
+                  float scale, int dtype, const void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  if (!q || !k || !v || !lse || !dO || !dk || !dv) return XATTN_ERR_NULL;
+  const int rc = check_bwd_common(B, S, H, Hkv, hd, scale, dtype, workspace, workspace_bytes);
+  if (rc != XATTN_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dO) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || !aligned4(lens))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_bwd_dkdv(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, lse, dO,
+                         static_cast<const float*>(workspace), dk, dv, lens, scale,
+                         static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dO, const int* lens, float* dq, float* dk, float* dv, int B, int S, int H,
+             int Hkv, int hd, float scale, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  // Validate everything up front so that an invalid call enqueues nothing.
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return XATTN_ERR_NULL;
+  int rc = check_bwd_common(B, S, H, Hkv, hd, scale, dtype, workspace, workspace_bytes);
+  if (rc != XATTN_OK) return rc;
+  if (!aligned16(dk) || !aligned16(dv)) return XATTN_ERR_ALIGN;
+  rc = bwd_dq_impl(q, k, v, o, lse, dO, lens, dq, B, S, H, Hkv, hd, scale, dtype, workspace,
+                   workspace_bytes, stream);
+  if (rc != XATTN_OK) return rc;
+  return bwd_dkdv_impl(q, k, v, lse, dO, lens, dk, dv, B, S, H, Hkv, hd, scale, dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+}  // namespace
+
 extern "C" {
 
 int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int S,
               int H, int Hkv, int hd, float scale, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse) return XATTN_ERR_NULL;
-  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
-  if (rc != XATTN_OK) return rc;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return XATTN_ERR_ALIGN;
-  xattn::launch_fwd(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, o, lse, scale,
-                    static_cast<hipStream_t>(stream));
-  return launch_status();
+  return fwd_impl(q, k, v, nullptr, o, lse, B, S, H, Hkv, hd, scale, dtype, stream);
 }
 
 size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype) {
@@ -68,54 +130,54 @@ size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dO, float* dq, int B, int S, int H, int Hkv, int hd, float scale,
                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !lse || !dO || !dq) return XATTN_ERR_NULL;
-  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
-  if (rc != XATTN_OK) return rc;
-  if (!workspace || workspace_bytes < xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype))
-    return XATTN_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-      !aligned16(dO) || !aligned16(dq) || !aligned16(workspace))
-    return XATTN_ERR_ALIGN;
-  xattn::launch_bwd_dq(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, o, lse, dO, dq,
-                       static_cast<float*>(workspace), scale, static_cast<hipStream_t>(stream));
-  return launch_status();
+  return bwd_dq_impl(q, k, v, o, lse, dO, nullptr, dq, B, S, H, Hkv, hd, scale, dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                    const void* dO, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
                    float scale, int dtype, const void* workspace, size_t workspace_bytes,
                    void* stream) {
-  if (!q || !k || !v || !lse || !dO || !dk || !dv) return XATTN_ERR_NULL;
-  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
-  if (rc != XATTN_OK) return rc;
-  if (!workspace || workspace_bytes < xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype))
-    return XATTN_ERR_WORKSPACE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(lse) || !aligned16(dO) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
-    return XATTN_ERR_ALIGN;
-  xattn::launch_bwd_dkdv(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, lse, dO,
-                         static_cast<const float*>(workspace), dk, dv, scale,
-                         static_cast<hipStream_t>(stream));
-  return launch_status();
+  return bwd_dkdv_impl(q, k, v, lse, dO, nullptr, dk, dv, B, S, H, Hkv, hd, scale, dtype,
+                       workspace, workspace_bytes, stream);
 }
 
 int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
               const void* dO, float* dq, float* dk, float* dv, int B, int S, int H, int Hkv,
               int hd, float scale, int dtype, void* workspace, size_t workspace_bytes,
               void* stream) {
-  // Validate everything up front so that an invalid call enqueues nothing.
-  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return XATTN_ERR_NULL;
-  int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  return bwd_impl(q, k, v, o, lse, dO, nullptr, dq, dk, dv, B, S, H, Hkv, hd, scale, dtype,
+                  workspace, workspace_bytes, stream);
+}
+
+int xattn_fwd_ragged(const void* q, const void* k, const void* v, const int* lens, void* o,
+                     float* lse, int B, int S, int H, int Hkv, int hd, float scale, int dtype,
+                     void* stream) {
+  if (!lens) return XATTN_ERR_NULL;
+  return fwd_impl(q, k, v, lens, o, lse, B, S, H, Hkv, hd, scale, dtype, stream);
+}
+
+int xattn_bwd_ragged(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, const int* lens, float* dq, float* dk, float* dv, int B,
+                     int S, int H, int Hkv, int hd, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!lens) return XATTN_ERR_NULL;
+  return bwd_impl(q, k, v, o, lse, dO, lens, dq, dk, dv, B, S, H, Hkv, hd, scale, dtype,
+                  workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+int check_bwd_common(int B, int S, int H, int Hkv, int hd, float scale, int dtype,
+                     const void* workspace, size_t workspace_bytes) {
+  const int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
   if (rc != XATTN_OK) return rc;
   if (!workspace || workspace_bytes < xattn_bwd_workspace_bytes(B, S, H, Hkv, hd, dtype))
     return XATTN_ERR_WORKSPACE;
-  if (!aligned16(dk) || !aligned16(dv)) return XATTN_ERR_ALIGN;
-  rc = xattn_bwd_dq(q, k, v, o, lse, dO, dq, B, S, H, Hkv, hd, scale, dtype, workspace,
-                    workspace_bytes, stream);
-  if (rc != XATTN_OK) return rc;
-  return xattn_bwd_dkdv(q, k, v, lse, dO, dk, dv, B, S, H, Hkv, hd, scale, dtype, workspace,
-                        workspace_bytes, stream);
+  return XATTN_OK;
 }
+}  // namespace
 
 namespace {
 int check_norm(int B, int S, int H, int hd, float eps, float base, int dtype) {
@@ -128,6 +190,8 @@ int check_norm(int B, int S, int H, int hd, float eps, float base, int dtype) {
   return XATTN_OK;
 }
 }  // namespace
+
+extern "C" {
 
 int xattn_qknorm_rope_fwd(const void* x, const float* w, void* out, int B, int S, int H, int hd,
                           float eps, float rope_base, int dtype, void* stream) {

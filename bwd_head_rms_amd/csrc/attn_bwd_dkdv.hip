@@ -40,8 +40,8 @@ template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ dws,
-    float* __restrict__ dk, float* __restrict__ dv, int B, int S, int H, int Hkv, int nkt,
-    int BG, float c, float scale) {
+    float* __restrict__ dk, float* __restrict__ dv, const int* __restrict__ lens, int B, int S,
+    int H, int Hkv, int nkt, int BG, float c, float scale) {
   using C = DkvCfg<T, HD>;
   using M = Mma<T>;
   __shared__ __align__(16) T sQ[2][C::TILE];
@@ -57,11 +57,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int b = bg / Hkv, kvh = bg % Hkv;
   const int group = H / Hkv;
   const size_t kvplane = ((size_t)b * Hkv + kvh) * S * HD;
+  const int n = seq_len(lens, b, S);  // rows and keys past n are padding
+  if (kt * C::BN >= n) {              // a tile of padding keys only: dk = dv = 0
+    for (int r = tid; r < C::BN; r += C::NT)
+      if (kt * C::BN + r < S) {
+        zero_row<HD>(dk + kvplane + (size_t)(kt * C::BN + r) * HD);
+        zero_row<HD>(dv + kvplane + (size_t)(kt * C::BN + r) * HD);
+      }
+    return;
+  }
 
   const int kv0 = kt * C::BN + wave * 32;
   const int my_kv = kv0 + li;
-  const bool kv_ok = my_kv < S;
-  const bool wave_live = kv0 < S;
+  const bool kv_ok = my_kv < n;
+  const bool wave_live = kv0 < n;
 
   typename M::frag kf[C::NKS], vf[C::NKS];
 #pragma unroll
@@ -85,7 +94,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   };
 
   const int qt_first = (kt * C::BN) / C::BMQ;
-  const int nq = (S + C::BMQ - 1) / C::BMQ;
+  const int nq = (n + C::BMQ - 1) / C::BMQ;  // query tiles holding rows of the sequence
   const int per_head = nq - qt_first;
   const int iters = group * per_head;
 
@@ -97,12 +106,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const int r = it / per_head, qt = qt_first + it % per_head;
     const size_t bh = (size_t)b * H + (size_t)kvh * group + r;
     const int row0 = qt * C::BMQ;
-    stQ.issue(q + bh * S * HD, row0, S, sQ[buf], wave, lane, tid);
-    stO.issue(dO + bh * S * HD, row0, S, sO[buf], wave, lane, tid);
-    // per-row statistics: 64 rows per wave instruction, rows past S read zero
+    // rows past n (padding, or past S) read zero: their Q, dO, LSE and D are
+    // zero, so they add exactly zero to dV (P * dO) and dK (dS * Q)
+    stQ.issue(q + bh * S * HD, row0, n, sQ[buf], wave, lane, tid);
+    stO.issue(dO + bh * S * HD, row0, n, sO[buf], wave, lane, tid);
+    // per-row statistics: 64 rows per wave instruction
     constexpr int NST = C::BMQ / kWave;
-    const v4i rl = make_rsrc(lse2 + bh * S, (uint32_t)S * 4u);
-    const v4i rd = make_rsrc(dws + bh * S, (uint32_t)S * 4u);
+    const v4i rl = make_rsrc(lse2 + bh * S, (uint32_t)n * 4u);
+    const v4i rd = make_rsrc(dws + bh * S, (uint32_t)n * 4u);
 #pragma unroll
     for (int i = 0; i < NST; ++i) {
       if (wave == i) {
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
           float p = fast_exp2(fmaf(s[r], c, -tL[ql]));
           if constexpr (MASK) {
             const int qi = qb0 + acc_row(r, g);
-            p = (qi >= my_kv && qi < S) ? p : 0.f;
+            p = (qi >= my_kv && qi < n) ? p : 0.f;
           }
           s[r] = p;
           dp[r] = p * (dp[r] + tD[ql]);  // dS (the workspace holds -D)
@@ -167,7 +178,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       };
 
       const int qt0 = qt * C::BMQ;
-      if (qt0 >= kv0 + 32 && qt0 + C::BMQ <= S) {
+      if (qt0 >= kv0 + 32 && qt0 + C::BMQ <= n) {
         // Every block of the tile is below the diagonal and inside the
         // sequence.  Phases are pinned with scheduling barriers so that each
         // LDS operand is read a whole phase before the instruction that needs
@@ -259,8 +270,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
           const int qb0 = qt0 + 32 * qb;
-          if (qb0 + 31 < kv0 || qb0 >= S) continue;  // wholly above the diagonal, or past S
-          if (qb0 < kv0 + 32 || qb0 + 32 > S)
+          if (qb0 + 31 < kv0 || qb0 >= n) continue;  // wholly above the diagonal, or past n
+          if (qb0 < kv0 + 32 || qb0 + 32 > n)
             block(qb, std::true_type{});
           else
             block(qb, std::false_type{});
@@ -272,7 +283,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   }
 
   if constexpr (sizeof(T) == 2) mma_agpr_drain();
-  if (!wave_live || !kv_ok) return;
+  if (!kv_ok) {  // padding keys inside the sequence's last tile
+    if (g == 0 && my_kv < S) {
+      zero_row<HD>(dk + kvplane + (size_t)my_kv * HD);
+      zero_row<HD>(dv + kvplane + (size_t)my_kv * HD);
+    }
+    return;
+  }
   float* krow = dk + kvplane + (size_t)my_kv * HD;
   float* vrow = dv + kvplane + (size_t)my_kv * HD;
 #pragma unroll
@@ -292,27 +309,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 template <typename T, int HD>
 static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* v,
                        const float* lse, const void* dO, const float* dws, float* dk, float* dv,
-                       float scale, hipStream_t stream) {
+                       const int* lens, float scale, hipStream_t stream) {
   using C = DkvCfg<T, HD>;
   const int nkt = (d.S + C::BN - 1) / C::BN;
   const int BG = d.B * d.Hkv;
   dim3 grid((unsigned)(nkt * BG)), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
-                     (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, d.B, d.S, d.H,
-                     d.Hkv, nkt, BG, scale * kLog2e, scale);
+                     (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, lens, d.B, d.S,
+                     d.H, d.Hkv, nkt, BG, scale * kLog2e, scale);
 }
 
 void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,
                      const float* lse, const void* dO, const float* dws, float* dk, float* dv,
-                     float scale, hipStream_t stream) {
+                     const int* lens, float scale, hipStream_t stream) {
   if (dtype == 0) {
-    if (d.hd == 16) dkdv_typed<float, 16>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
-    else if (d.hd == 32) dkdv_typed<float, 32>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
-    else dkdv_typed<float, 64>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+    if (d.hd == 16) dkdv_typed<float, 16>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
+    else if (d.hd == 32) dkdv_typed<float, 32>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
+    else dkdv_typed<float, 64>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
   } else {
-    if (d.hd == 16) dkdv_typed<bf16, 16>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
-    else if (d.hd == 32) dkdv_typed<bf16, 32>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
-    else dkdv_typed<bf16, 64>(d, q, k, v, lse, dO, dws, dk, dv, scale, stream);
+    if (d.hd == 16) dkdv_typed<bf16, 16>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
+    else if (d.hd == 32) dkdv_typed<bf16, 32>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
+    else dkdv_typed<bf16, 64>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
   }
 }
 

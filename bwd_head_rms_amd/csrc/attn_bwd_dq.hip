@@ -36,8 +36,8 @@ template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ o, const float* __restrict__ lse, const T* __restrict__ dO,
-    float* __restrict__ dq, float* __restrict__ dws, int S, int H, int Hkv, int nqt, int BH,
-    float c, float scale) {
+    float* __restrict__ dq, float* __restrict__ dws, const int* __restrict__ lens, int S, int H,
+    int Hkv, int nqt, int BH, float c, float scale) {
   using C = DqCfg<T, HD>;
   using M = Mma<T>;
   __shared__ __align__(16) T sK[2][C::TILE];
@@ -53,12 +53,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const size_t qplane = (size_t)bh * S * HD;
   const T* kp = k + ((size_t)b * Hkv + kvh) * S * HD;
   const T* vp = v + ((size_t)b * Hkv + kvh) * S * HD;
+  const int n = seq_len(lens, b, S);  // rows and keys past n are padding
+  if (qt * C::BM >= n) {              // a tile of padding only: dq = 0
+    for (int r = tid; r < C::BM; r += C::NT)
+      if (qt * C::BM + r < S) zero_row<HD>(dq + qplane + (size_t)(qt * C::BM + r) * HD);
+    return;
+  }
 
   const int q0 = qt * C::BM + wave * 32;
   const int my_q = q0 + li;
-  const bool q_ok = my_q < S;
-  const bool wave_live = q0 < S;
-  const int wave_kv_end = min(S, q0 + 32);
+  const bool q_ok = my_q < n;
+  const bool wave_live = q0 < n;
+  const int wave_kv_end = min(n, q0 + 32);
 
   typename M::frag qf[C::NKS], df[C::NKS];
   float Dp = 0.f;
@@ -94,13 +100,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) negD[r] = -Drow;
 
-  const int kv_end = min(S, qt * C::BM + C::BM);
+  const int kv_end = min(n, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
   wait_global_loads();  // the per-row operands above are in registers
   Stager<T, HD, C::BN, C::NW> stK, stV;
-  stK.issue(kp, 0, S, sK[0], wave, lane, tid);
-  stV.issue(vp, 0, S, sV[0], wave, lane, tid);
+  stK.issue(kp, 0, n, sK[0], wave, lane, tid);
+  stV.issue(vp, 0, n, sV[0], wave, lane, tid);
   wait_global_loads();
   stK.commit(sK[0], tid);
   stV.commit(sV[0], tid);
@@ -111,8 +117,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const int kv_t0 = j * C::BN;
     const bool more = j + 1 < ntiles;
     if (more) {  // the other buffer was last read before the previous barrier
-      stK.issue(kp, kv_t0 + C::BN, S, sK[cur ^ 1], wave, lane, tid);
-      stV.issue(vp, kv_t0 + C::BN, S, sV[cur ^ 1], wave, lane, tid);
+      stK.issue(kp, kv_t0 + C::BN, n, sK[cur ^ 1], wave, lane, tid);
+      stV.issue(vp, kv_t0 + C::BN, n, sV[cur ^ 1], wave, lane, tid);
     }
     if (wave_live && kv_t0 < wave_kv_end) {
       const T* tK = sK[cur];
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
           float p = fast_exp2(fmaf(s[r], c, -lse2));
           if constexpr (MASK) {
             const int kv = kb0 + acc_row(r, g);
-            p = (kv <= my_q && kv < S) ? p : 0.f;
+            p = (kv <= my_q && kv < n) ? p : 0.f;
           }
           s[r] = p * dp[r];  // dS^T = P (dP - D)
         }
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       for (int cb = 0; cb < C::NB; ++cb) {
         const int kb0 = kv_t0 + 32 * cb;
         if (kb0 >= wave_kv_end) continue;  // wholly above this wave's rows, or past S
-        if (kb0 + 31 > q0 || kb0 + 32 > S)
+        if (kb0 + 31 > q0 || kb0 + 32 > n)
           block(cb, std::true_type{});
         else
           block(cb, std::false_type{});
@@ -166,7 +172,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     __syncthreads();
   }
 
-  if (!wave_live || !q_ok) return;
+  if (!q_ok) {  // padding rows inside the sequence's last tile
+    if (g == 0 && my_q < S) zero_row<HD>(dq + qplane + (size_t)my_q * HD);
+    return;
+  }
   float* qrow = dq + qplane + (size_t)my_q * HD;
 #pragma unroll
   for (int db = 0; db < C::ND; ++db)
@@ -181,28 +190,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 
 template <typename T, int HD>
 static void dq_typed(const Dims& d, const void* q, const void* k, const void* v, const void* o,
-                     const float* lse, const void* dO, float* dq, float* dws, float scale,
-                     hipStream_t stream) {
+                     const float* lse, const void* dO, float* dq, float* dws, const int* lens,
+                     float scale, hipStream_t stream) {
   using C = DqCfg<T, HD>;
   const int nqt = (d.S + C::BM - 1) / C::BM;
   const int BH = d.B * d.H;
   dim3 grid((unsigned)(nqt * BH)), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)o, lse, (const T*)dO, dq, dws, d.S, d.H,
-                     d.Hkv, nqt, BH, scale * kLog2e, scale);
+                     (const T*)k, (const T*)v, (const T*)o, lse, (const T*)dO, dq, dws, lens, d.S,
+                     d.H, d.Hkv, nqt, BH, scale * kLog2e, scale);
 }
 
 void launch_bwd_dq(int dtype, const Dims& d, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, const void* dO, float* dq, float* dws,
-                   float scale, hipStream_t stream) {
+                   const int* lens, float scale, hipStream_t stream) {
   if (dtype == 0) {
-    if (d.hd == 16) dq_typed<float, 16>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
-    else if (d.hd == 32) dq_typed<float, 32>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
-    else dq_typed<float, 64>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+    if (d.hd == 16) dq_typed<float, 16>(d, q, k, v, o, lse, dO, dq, dws, lens, scale, stream);
+    else if (d.hd == 32) dq_typed<float, 32>(d, q, k, v, o, lse, dO, dq, dws, lens, scale, stream);
+    else dq_typed<float, 64>(d, q, k, v, o, lse, dO, dq, dws, lens, scale, stream);
   } else {
-    if (d.hd == 16) dq_typed<bf16, 16>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
-    else if (d.hd == 32) dq_typed<bf16, 32>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
-    else dq_typed<bf16, 64>(d, q, k, v, o, lse, dO, dq, dws, scale, stream);
+    if (d.hd == 16) dq_typed<bf16, 16>(d, q, k, v, o, lse, dO, dq, dws, lens, scale, stream);
+    else if (d.hd == 32) dq_typed<bf16, 32>(d, q, k, v, o, lse, dO, dq, dws, lens, scale, stream);
+    else dq_typed<bf16, 64>(d, q, k, v, o, lse, dO, dq, dws, lens, scale, stream);
   }
 }
 

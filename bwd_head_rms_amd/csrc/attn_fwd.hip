@@ -33,6 +33,23 @@ namespace xattn {
 // row sum l below 2^64 * S, so no precision or range is lost.
 constexpr float kRescaleBound = 18446744073709551616.f;  // 2^64
 
+// A padding row of the output: o = 0, lse = -inf (nothing to attend to).
+template <typename T, int HD>
+__device__ __forceinline__ void store_padding_row(T* o, float* lse, int bh, int S, int row) {
+  T* orow = o + ((size_t)bh * S + row) * HD;
+#pragma unroll
+  for (int d = 0; d < HD; d += 4) store4<T>(orow + d, 0.f, 0.f, 0.f, 0.f);
+  lse[(size_t)bh * S + row] = -INFINITY;
+}
+
+// Rows [row0, row0 + rows) of (b, h) that lie inside the tensor, all padding.
+template <typename T, int HD>
+__device__ __forceinline__ void store_padding_rows(T* o, float* lse, int bh, int S, int row0,
+                                                   int rows, int tid, int nt) {
+  for (int r = tid; r < rows; r += nt)
+    if (row0 + r < S) store_padding_row<T, HD>(o, lse, bh, S, row0 + r);
+}
+
 template <typename T, int HD>
 struct FwdCfg {
   static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
@@ -45,7 +62,8 @@ struct FwdCfg {
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    T* __restrict__ o, float* __restrict__ lse, int S, int H, int Hkv, int nqt, int BH, float c) {
+    T* __restrict__ o, float* __restrict__ lse, const int* __restrict__ lens, int S, int H,
+    int Hkv, int nqt, int BH, float c) {
   using C = FwdCfg<T, HD>;
   using M = Mma<T>;
   __shared__ __align__(16) T sK[2][C::TILE];
@@ -61,12 +79,19 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   const T* qp = q + (size_t)bh * S * HD;
   const T* kp = k + ((size_t)b * Hkv + kvh) * S * HD;
   const T* vp = v + ((size_t)b * Hkv + kvh) * S * HD;
+  const int n = seq_len(lens, b, S);  // rows and keys past n are padding
+  if (qt * C::BM >= n) {              // a tile of padding only
+    store_padding_rows<T, HD>(o, lse, bh, S, qt * C::BM, C::BM, tid, C::NT);
+    return;
+  }
 
   const int q0 = qt * C::BM + wave * 32;
   const int my_q = q0 + li;
-  const bool q_ok = my_q < S;
-  const bool wave_live = q0 < S;
-  const int wave_kv_end = min(S, q0 + 32);  // keys visible to some row of this wave
+  const bool q_ok = my_q < n;
+  const bool wave_live = q0 < n;
+  const int wave_kv_end = min(n, q0 + 32);  // keys visible to some row of this wave
+  // padding rows of this tile are written first, while nothing is live
+  if (!q_ok && g == 0 && my_q < S) store_padding_row<T, HD>(o, lse, bh, S, my_q);
 
   typename M::frag qf[C::NKS];
 #pragma unroll
@@ -78,13 +103,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   for (int d = 0; d < C::ND; ++d) oacc[d] = zero_acc();
   float m = -INFINITY, l = 0.f;
 
-  const int kv_end = min(S, qt * C::BM + C::BM);
+  const int kv_end = min(n, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
   wait_global_loads();  // the query operand above is in registers
   Stager<T, HD, C::BN, C::NW> stK, stV;
-  stK.issue(kp, 0, S, sK[0], wave, lane, tid);
-  stV.issue(vp, 0, S, sV[0], wave, lane, tid);
+  stK.issue(kp, 0, n, sK[0], wave, lane, tid);
+  stV.issue(vp, 0, n, sV[0], wave, lane, tid);
   wait_global_loads();
   stK.commit(sK[0], tid);
   stV.commit(sV[0], tid);
@@ -95,8 +120,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     const int kv_t0 = j * C::BN;
     const bool more = j + 1 < ntiles;
     if (more) {  // the other buffer was last read before the previous barrier
-      stK.issue(kp, kv_t0 + C::BN, S, sK[cur ^ 1], wave, lane, tid);
-      stV.issue(vp, kv_t0 + C::BN, S, sV[cur ^ 1], wave, lane, tid);
+      stK.issue(kp, kv_t0 + C::BN, n, sK[cur ^ 1], wave, lane, tid);
+      stV.issue(vp, kv_t0 + C::BN, n, sV[cur ^ 1], wave, lane, tid);
     }
     if (wave_live && kv_t0 < wave_kv_end) {
       const T* tK = sK[cur];
@@ -118,11 +143,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 #pragma unroll
             for (int ks = 0; ks < C::NKS; ++ks)
               M::mma(s[cb], row_frag_lds<T, HD, C::BN>(tK, 32 * cb + li, g, ks), qf[ks]);
-            if (kb0 + 31 > q0 || kb0 + 32 > S) {
+            if (kb0 + 31 > q0 || kb0 + 32 > n) {
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int kv = kb0 + acc_row(r, g);
-                s[cb][r] = (kv <= my_q && kv < S) ? s[cb][r] : -INFINITY;
+                s[cb][r] = (kv <= my_q && kv < n) ? s[cb][r] : -INFINITY;
               }
             }
           }
@@ -193,7 +218,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     __syncthreads();
   }
 
-  if (!wave_live) return;
+  if (!wave_live) return;  // a wave of padding rows (stored at the start)
   l = halves_sum(l);
   const float inv = 1.f / l;
   if (q_ok) {
@@ -253,8 +278,8 @@ constexpr float kHalfBlockBound = 9223372036854775808.f;  // 2^63
 template <int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_fwd_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    bf16* __restrict__ o, float* __restrict__ lse, int S, int H, int Hkv, int nqt, int BH,
-    float c) {
+    bf16* __restrict__ o, float* __restrict__ lse, const int* __restrict__ lens, int S, int H,
+    int Hkv, int nqt, int BH, float c) {
   using P = FwdPipe<HD>;
   using M = Mma<bf16>;
   using frag = M::frag;
@@ -271,16 +296,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int kvh = h / (H / Hkv);
   const bf16* qp = q + (size_t)bh * S * HD;
   const size_t kvoff = ((size_t)b * Hkv + kvh) * S * HD;
+  const int n = seq_len(lens, b, S);  // rows and keys past n are padding
+  if (qt * P::BM >= n) {              // a tile of padding only
+    store_padding_rows<bf16, HD>(o, lse, bh, S, qt * P::BM, P::BM, tid, P::NT);
+    return;
+  }
 
   const int q0 = qt * P::BM + wave * 32;
   const int my_q = q0 + li;
-  const bool q_ok = my_q < S;
+  const bool q_ok = my_q < n;
   // Blocks of the workgroup and of this wave; a wave's last block is its
-  // diagonal block, which also holds the end of the sequence when S is ragged.
-  // A wave wholly past the end (last tile of a ragged sequence) runs over all
-  // blocks like a live one and stores nothing.
-  const int nbw = (min(S, qt * P::BM + P::BM) + 31) / 32;
-  const int nb = (min(S, q0 + 32) + 31) / 32;
+  // diagonal block, which also holds the end of the sequence when n is not a
+  // multiple of 32.  A wave wholly past the end (last tile of a sequence) runs
+  // over all blocks like a live one and stores padding rows.
+  const int nbw = (min(n, qt * P::BM + P::BM) + 31) / 32;
+  const int nb = (min(n, q0 + 32) + 31) / 32;
+  // padding rows of this tile are written first, while nothing is live
+  if (!q_ok && g == 0 && my_q < S) store_padding_row<bf16, HD>(o, lse, bh, S, my_q);
 
   f32x16 oacc[P::ND];
 #pragma unroll
@@ -291,7 +323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // Copies: wave w < NINST copies rows w*RPI .. +RPI-1 of a block; a block past
   // the workgroup's last one is addressed past the end of the plane and reads
   // zero without a memory access.
-  const uint32_t plane_bytes = (uint32_t)S * HD * 2u;
+  const uint32_t plane_bytes = (uint32_t)n * HD * 2u;  // keys past n read zero
   const v4i rK = make_rsrc(k + kvoff, plane_bytes);
   const v4i rV = make_rsrc(v + kvoff, plane_bytes);
   const int crow = wave * P::RPI + lane / P::CPR;
@@ -336,7 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kv = kb0 + acc_row(r, g);
-      s[r] = (kv <= my_q && kv < S) ? s[r] : -INFINITY;
+      s[r] = (kv <= my_q && kv < n) ? s[r] : -INFINITY;
     }
   };
 
@@ -419,7 +451,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (2 * u + 2 >= nbw) break;
   }
 
-  if (q0 >= S) return;
+  if (q0 >= n) return;  // a wave of padding rows (stored at the start)
   const bool row_bad = halves_max(bad ? 1.f : 0.f) != 0.f;
   if (__builtin_expect(__ballot(row_bad) != 0, 0)) {
     // exact recompute of this wave's rows from HBM: running max, rescale per
@@ -435,13 +467,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       f32x16 s2 = zero_acc();
 #pragma unroll
       for (int ks = 0; ks < P::NKS; ++ks)
-        M::mma(s2, key < S ? row_frag_global<bf16, HD>(kp + (size_t)key * HD, g, ks) : zero_frag<bf16>(),
+        M::mma(s2, key < n ? row_frag_global<bf16, HD>(kp + (size_t)key * HD, g, ks) : zero_frag<bf16>(),
                qf[ks]);
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kv = 32 * j + acc_row(r, g);
-        s2[r] = (kv <= my_q && kv < S) ? s2[r] : -INFINITY;
+        s2[r] = (kv <= my_q && kv < n) ? s2[r] : -INFINITY;
         mx = fmaxf(mx, s2[r]);
       }
       const float m_new = fmaxf(m2, halves_max(mx) * c);
@@ -467,7 +499,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             const int kv = 32 * j + acc_row(8 * ks + t, g);
-            vf[t] = kv < S ? vp[(size_t)kv * HD + d] : (bf16)0.f;
+            vf[t] = kv < n ? vp[(size_t)kv * HD + d] : (bf16)0.f;
           }
           M::mma(acc2[db], vf, p2[ks]);
         }
@@ -499,38 +531,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
 template <typename T, int HD>
 static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v, void* o,
-                      float* lse, float scale, hipStream_t stream) {
+                      float* lse, const int* lens, float scale, hipStream_t stream) {
   using C = FwdCfg<T, HD>;
   const int nqt = (d.S + C::BM - 1) / C::BM;
   const int BH = d.B * d.H;
   dim3 grid((unsigned)(nqt * BH)), block(C::NT);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, block, 0, stream,
-                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, d.S, d.H, d.Hkv, nqt, BH,
-                     scale * kLog2e);
+                     (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, lens, d.S, d.H, d.Hkv,
+                     nqt, BH, scale * kLog2e);
 }
 
 template <int HD>
 static void fwd_pipe(const Dims& d, const void* q, const void* k, const void* v, void* o,
-                     float* lse, float scale, hipStream_t stream) {
+                     float* lse, const int* lens, float scale, hipStream_t stream) {
   using P = FwdPipe<HD>;
   const int nqt = (d.S + P::BM - 1) / P::BM;
   const int BH = d.B * d.H;
   dim3 grid((unsigned)(nqt * BH)), block(P::NT);
   hipLaunchKernelGGL((attn_fwd_pipe_kernel<HD>), grid, block, 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, d.S, d.H,
-                     d.Hkv, nqt, BH, scale * kLog2e);
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, lens, d.S,
+                     d.H, d.Hkv, nqt, BH, scale * kLog2e);
 }
 
 void launch_fwd(int dtype, const Dims& d, const void* q, const void* k, const void* v, void* o,
-                float* lse, float scale, hipStream_t stream) {
+                float* lse, const int* lens, float scale, hipStream_t stream) {
   if (dtype == 0) {
-    if (d.hd == 16) fwd_typed<float, 16>(d, q, k, v, o, lse, scale, stream);
-    else if (d.hd == 32) fwd_typed<float, 32>(d, q, k, v, o, lse, scale, stream);
-    else fwd_typed<float, 64>(d, q, k, v, o, lse, scale, stream);
+    if (d.hd == 16) fwd_typed<float, 16>(d, q, k, v, o, lse, lens, scale, stream);
+    else if (d.hd == 32) fwd_typed<float, 32>(d, q, k, v, o, lse, lens, scale, stream);
+    else fwd_typed<float, 64>(d, q, k, v, o, lse, lens, scale, stream);
   } else {
-    if (d.hd == 16) fwd_pipe<16>(d, q, k, v, o, lse, scale, stream);
-    else if (d.hd == 32) fwd_pipe<32>(d, q, k, v, o, lse, scale, stream);
-    else fwd_pipe<64>(d, q, k, v, o, lse, scale, stream);
+    if (d.hd == 16) fwd_pipe<16>(d, q, k, v, o, lse, lens, scale, stream);
+    else if (d.hd == 32) fwd_pipe<32>(d, q, k, v, o, lse, lens, scale, stream);
+    else fwd_pipe<64>(d, q, k, v, o, lse, lens, scale, stream);
   }
 }
 

@@ -9,19 +9,23 @@ struct Dims {
   int B, S, H, Hkv, hd;
 };
 
+// `lens` ([B] int32 on the device, or NULL): sequence b holds lens[b] rows
+// (clamped to [0, S]) of its right-padded S-row planes; rows and keys past it
+// are padding, never read, and their outputs are written as zeros (lse -inf).
+
 // Forward: o, lse from q, k, v.  dtype: 0 = fp32, 1 = bf16.
 void launch_fwd(int dtype, const Dims& d, const void* q, const void* k, const void* v, void* o,
-                float* lse, float scale, hipStream_t stream);
+                float* lse, const int* lens, float scale, hipStream_t stream);
 
 // Backward, first kernel: dq, and D = rowsum(dO * o) into `dws` ([B][H][S] float).
 void launch_bwd_dq(int dtype, const Dims& d, const void* q, const void* k, const void* v,
                    const void* o, const float* lse, const void* dO, float* dq, float* dws,
-                   float scale, hipStream_t stream);
+                   const int* lens, float scale, hipStream_t stream);
 
 // Backward, second kernel: dk, dv (group-summed), reading D from `dws`.
 void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,
                      const float* lse, const void* dO, const float* dws, float* dk, float* dv,
-                     float scale, hipStream_t stream);
+                     const int* lens, float scale, hipStream_t stream);
 
 // Per-head RMS QK-norm + rotary embedding.  x [B][S][H][hd] (token-major),
 // out and dout [B][H][S][hd], dx [B][S][H][hd], w and dw [hd].

@@ -140,6 +140,35 @@ def generate_workload(w):
 
 
 @dataclass(frozen=True)
+class RaggedWorkload:
+    """A right-padded batch: B sequences with lengths drawn uniformly from
+    [min_len, S] (seeded), padded to S, in the long-context workload's head
+    shape.  The pages train on variable-length sequences batched by right
+    padding; this length mix stands in for their data."""
+    name: str
+    B: int
+    S: int
+    H: int
+    Hkv: int
+    hd: int
+    dtype: str
+    seed: int
+    min_len: int
+
+    @property
+    def scale(self):
+        return 1.0 / float(np.sqrt(self.hd))
+
+    def lens(self):
+        return [int(x) for x in
+                np.random.default_rng(self.seed).integers(self.min_len, self.S + 1, self.B)]
+
+
+RAGGED_BENCH = RaggedWorkload("ragged_b8_s2048_h16_hd64_bf16_len256to2048", 8, 2048, 16, 16, 64,
+                              "bf16", 7, 256)
+
+
+@dataclass(frozen=True)
 class DecodeWorkload:
     """One decode step: a new query per (sequence, head) against a K/V cache of T
     positions.  ``source`` names the attention workload whose last query row

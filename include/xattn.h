@@ -185,6 +185,31 @@ int xattn_qknorm_rope_bwd(const void* x, const float* w, const float* dout, floa
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Right-padded batches with per-sequence lengths (the pad-and-mask batching of
+ * the "xtrain evolution overview" page, post-training stage, milestone M2d:
+ * sequences of different lengths are right-padded to one length S; under the
+ * causal mask a real row never sees a later padding position, so its output
+ * equals the unpadded sequence's).  Same operation, layout and rules as
+ * xattn_fwd / xattn_bwd, plus
+ *   lens  [B] int32 device array: sequence b holds rows 0 .. lens[b]-1 of its
+ *         S-row planes (values clamped to [0, S] on the device).
+ * For each sequence the result on its rows equals xattn_fwd / xattn_bwd of
+ * that sequence alone (S = lens[b]); padding rows and keys are never read (they
+ * may hold anything, NaN included) and are written as o = 0, lse = -inf,
+ * dq = dk = dv = 0.  Work on tiles that hold only padding is skipped.
+ * lens must be 4-byte aligned; it is required (NULL -> XATTN_ERR_NULL).
+ * The workspace is the one xattn_bwd_workspace_bytes sizes.
+ */
+int xattn_fwd_ragged(const void* q, const void* k, const void* v, const int* lens, void* o,
+                     float* lse, int B, int S, int H, int Hkv, int hd, float scale, int dtype,
+                     void* stream);
+
+int xattn_bwd_ragged(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, const int* lens, float* dq, float* dk, float* dv, int B,
+                     int S, int H, int Hkv, int hd, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * Decode attention: the new query of each sequence against that sequence's
  * key/value cache (the decode-attention primitive of the "xtrain evolution
  * overview" page, post-training stage: milestone M2a -- one query against the

@@ -115,6 +115,34 @@ class Oracle:
         return out
 
 
+    # -- right-padded batch ----------------------------------------------------
+    def run_ragged(self, q, k, v, lens, dO=None, scale=None, backward=True):
+        """Right-padded batch with per-sequence lengths: sequence b holds rows
+        0 .. lens[b]-1 of its S-row planes.  Its rows are the plain causal
+        attention of that prefix alone (``run`` on the prefix); padding rows
+        are o = 0, lse = -inf, dq = dk = dv = 0, and padding inputs are never
+        read.  (The pages batch sequences of different lengths by right
+        padding: "xtrain evolution overview", post-training stage, M2d.)"""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, H, S, hd = q.shape
+        bwd = backward and dO is not None
+        out = {"o": np.zeros(q.shape), "lse": np.full((B, H, S), -np.inf)}
+        if bwd:
+            dO = _f64(dO)
+            out.update(dq=np.zeros(q.shape), dk=np.zeros(k.shape), dv=np.zeros(k.shape))
+        for b, n in enumerate(lens):
+            n = int(n)
+            if n < 0 or n > S:
+                raise OracleError(f"length {n} outside [0, {S}]")
+            if n == 0:
+                continue
+            r = self.run(q[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n],
+                         dO[b:b + 1, :, :n] if bwd else None, scale=scale, backward=bwd)
+            for name, x in r.items():
+                out[name][b, :, :n] = x[0]
+        return out
+
+
 _default = None
 
 

@@ -242,3 +242,39 @@ def test_decode_workspace_bytes(L):
     # 8 x 4 units x 32 chunks of 1024 (group 4: one workgroup takes all 4 query heads)
     assert f(8, 32768, 16, 4, 64) == 4 * 8 * 16 * 32 * 66
     assert f(0, 16, 2, 2, 16) == 0 and f(1, 16, 3, 2, 16) == 0 and f(1, 16, 2, 2, 48) == 0
+
+
+# -- right-padded batches ----------------------------------------------------------
+def rfwd(L, lens=P, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, S=16, H=2, Hkv=2, hd=16, scale=0.25, dtype=0)
+    a.update(kw)
+    return L.xattn_fwd_ragged(a["q"], a["k"], a["v"], lens, a["o"], a["lse"], a["B"], a["S"],
+                              a["H"], a["Hkv"], a["hd"], a["scale"], a["dtype"], None)
+
+
+def rbwd(L, lens=P, ws=P, ws_bytes=None, **kw):
+    a = dict(B=1, S=16, H=2, Hkv=2, hd=16, scale=0.25, dtype=0)
+    p = {n: P for n in ("q", "k", "v", "o", "lse", "dO", "dq", "dk", "dv")}
+    for n in list(kw):
+        (p if n in p else a)[n] = kw[n]
+    if ws_bytes is None:
+        ws_bytes = 8 * a["B"] * a["H"] * a["S"]
+    return L.xattn_bwd_ragged(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], lens, p["dq"],
+                              p["dk"], p["dv"], a["B"], a["S"], a["H"], a["Hkv"], a["hd"],
+                              a["scale"], a["dtype"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lens=None), NULL), (dict(q=None), NULL), (dict(lse=None), NULL), (dict(B=0), SHAPE),
+    (dict(H=3, Hkv=2), GQA), (dict(hd=24), HEAD_DIM), (dict(dtype=7), DTYPE),
+    (dict(scale=-1.0), SCALE), (dict(lens=P + 2), ALIGN), (dict(o=P + 8), ALIGN)])
+def test_fwd_ragged_rejects(L, kw, status):
+    assert rfwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lens=None), NULL), (dict(dO=None), NULL), (dict(dv=None), NULL), (dict(S=0), SHAPE),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=8), WORKSPACE), (dict(lens=P + 1), ALIGN),
+    (dict(dk=P + 4), ALIGN), (dict(hd=128), HEAD_DIM)])
+def test_bwd_ragged_rejects(L, kw, status):
+    assert rbwd(L, **kw) == status
