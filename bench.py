@@ -24,9 +24,10 @@ reads x and the fp32 upstream gradient and writes the fp32 dx), and decode
 attention (one new query per sequence and head against a K/V cache) on a
 32768-position bf16 cache and on the long-context workload's last row, against
 the same bandwidth (algorithmic bytes: the cached K and V once, q, o and lse),
-and a right-padded batch of 8 sequences with lengths 256..2048 through the
-length-aware kernels, against the same batch run padded.  None of them is part
-of the timed attention step.
+a right-padded batch of 8 sequences with lengths 256..2048 through the
+length-aware kernels, against the same batch run padded, and the composed path
+(scores, softmax, products through S x S fp32 buffers) on the same workload as
+the step, with the memory it needs.  None of them is part of the timed step.
 
 Prints ONE JSON line.
 """
@@ -366,6 +367,64 @@ def run_ragged(rw, steps, warmup):
             "tokens_per_s": round(sum(lens) / (ms["ragged"] / 1e3), 1)}
 
 
+def run_composed(w, steps, warmup):
+    """Time the composed path (xattn_composed_fwd + _bwd: S x S fp32 buffers)
+    on workload `w`, for comparison with the fused step.  Counted FLOPs as the
+    headline (14*hd*nnz per (batch, head))."""
+    import torch
+
+    from bwd_head_rms_amd import _lib, inputs
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    arrs = inputs.generate_workload(w)
+    t = {n: inputs.to_torch(a, w.dtype, dev) for n, a in arrs.items()}
+    del arrs
+    code = _lib.BF16 if w.dtype == "bf16" else _lib.F32
+    nbuf = int(L.xattn_composed_buffer_bytes(w.B, w.S, w.H))
+    f32 = dict(dtype=torch.float32, device=dev)
+    p = torch.empty((nbuf // 4,), **f32)
+    ds = torch.empty((nbuf // 4,), **f32)
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((w.B, w.H, w.S), **f32)
+    dq = torch.empty(t["q"].shape, **f32)
+    dk = torch.empty(t["k"].shape, **f32)
+    dv = torch.empty(t["k"].shape, **f32)
+    sh = torch.cuda.current_stream(dev).cuda_stream
+    dims = (w.B, w.S, w.H, w.Hkv, w.hd, w.scale, code)
+
+    def fwd():
+        _lib.check(L.xattn_composed_fwd(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                        o.data_ptr(), lse.data_ptr(), p.data_ptr(), nbuf, *dims, sh))
+
+    def bwd():
+        _lib.check(L.xattn_composed_bwd(t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                        p.data_ptr(), nbuf, t["dO"].data_ptr(), dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), ds.data_ptr(), nbuf, *dims,
+                                        sh))
+
+    ms = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / steps
+    tot = ms["fwd"] + ms["bwd"]
+    tf = counted_flops(w)["total"] / (tot / 1e3) / 1e12
+    return {"workload": w.name, "fwd_ms": round(ms["fwd"], 4), "bwd_ms": round(ms["bwd"], 4),
+            "ms_per_step": round(tot, 4), "tflops": round(tf, 3),
+            "pct_of_mfma_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 3),
+            "s_by_s_buffers_bytes": 2 * nbuf,
+            "fused_workspace_bytes": int(L.xattn_bwd_workspace_bytes(w.B, w.S, w.H, w.Hkv, w.hd,
+                                                                     code))}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,11 +434,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip QK-norm + RoPE, decode and ragged batches ('next_rows')")
+                    help="skip QK-norm + RoPE, decode, ragged and composed ('next_rows')")
     ap.add_argument("--norm-only", action="store_true",
                     help="only time the QK-norm + RoPE step (for profiling its kernels)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time decode attention (for profiling its kernels)")
+    ap.add_argument("--composed-only", action="store_true",
+                    help="only time the composed path (for profiling its kernels)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (for counter calibration)")
     args = ap.parse_args()
@@ -397,6 +458,9 @@ def main():
     w = inputs.WORKLOADS[args.workload or inputs.LONG_CONTEXT]
     if args.norm_only:
         print(json.dumps({"qknorm_rope": run_norm(w, args.steps, args.warmup)}), flush=True)
+        return
+    if args.composed_only:
+        print(json.dumps({"composed": run_composed(w, args.steps, args.warmup)}), flush=True)
         return
     if args.decode_only:
         wd = inputs.DECODE_WORKLOADS[inputs.DECODE_BENCH]
@@ -455,7 +519,8 @@ def main():
             "decode_long_context_last_row": run_decode(
                 inputs.DECODE_WORKLOADS["decode_long_b4_t2048_h16_hd64_bf16"], args.steps,
                 args.warmup),
-            "ragged": run_ragged(inputs.RAGGED_BENCH, args.steps, args.warmup)}
+            "ragged": run_ragged(inputs.RAGGED_BENCH, args.steps, args.warmup),
+            "composed": run_composed(w, max(3, args.steps // 5), max(1, args.warmup // 5))}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)

@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so
 SYMBOLS = ("xattn_fwd", "xattn_bwd", "xattn_bwd_workspace_bytes", "xattn_bwd_dq",
            "xattn_bwd_dkdv", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
            "xattn_qknorm_rope_bwd", "xattn_decode_workspace_bytes", "xattn_decode",
-           "xattn_fwd_ragged", "xattn_bwd_ragged",
+           "xattn_fwd_ragged", "xattn_bwd_ragged", "xattn_composed_buffer_bytes",
+           "xattn_composed_fwd", "xattn_composed_bwd",
            "xattn_strerror")
 
 F32, BF16 = 0, 1
@@ -60,6 +61,12 @@ def lib():
     L.xattn_fwd_ragged.restype = i
     L.xattn_bwd_ragged.argtypes = [vp] * 10 + [i, i, i, i, i, f, i, vp, sz, vp]
     L.xattn_bwd_ragged.restype = i
+    L.xattn_composed_buffer_bytes.argtypes = [i, i, i]
+    L.xattn_composed_buffer_bytes.restype = sz
+    L.xattn_composed_fwd.argtypes = [vp] * 6 + [sz, i, i, i, i, i, f, i, vp]
+    L.xattn_composed_fwd.restype = i
+    L.xattn_composed_bwd.argtypes = [vp] * 4 + [sz] + [vp] * 5 + [sz, i, i, i, i, i, f, i, vp]
+    L.xattn_composed_bwd.restype = i
     L.xattn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.xattn_decode_workspace_bytes.restype = sz
     L.xattn_decode.argtypes = [vp] * 6 + [i, i, i, i, i, f, i, vp, sz, vp]

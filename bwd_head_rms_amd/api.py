@@ -211,3 +211,46 @@ def decode(q, k, v, lens=None, scale=None, o=None, lse=None, workspace=None):
                              lse.data_ptr(), B, T, H, Hkv, hd, scale, _code(q), wptr, wbytes,
                              _stream(q)))
     return o, lse
+
+
+def composed_buffer_bytes(B, S, H):
+    return int(lib().xattn_composed_buffer_bytes(B, S, H))
+
+
+def composed_fwd(q, k, v, scale=None, p=None):
+    """The composed path's forward (scores, causal softmax, P.V through an
+    S x S fp32 buffer).  Returns (o, lse, p) with p [B,H,S,S] fp32."""
+    B, S, H, Hkv, hd = _dims(q, k)
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check_tensor(q, "q", (B, H, S, hd), q.dtype)
+    _check_tensor(k, "k", (B, Hkv, S, hd), q.dtype)
+    _check_tensor(v, "v", (B, Hkv, S, hd), q.dtype)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    p = torch.empty((B, H, S, S), dtype=torch.float32, device=q.device) if p is None else p
+    _check_tensor(p, "p", (B, H, S, S), torch.float32)
+    check(lib().xattn_composed_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), p.data_ptr(), p.numel() * 4, B, S, H, Hkv, hd,
+                                   scale, _code(q), _stream(q)))
+    return o, lse, p
+
+
+def composed_bwd(q, k, v, p, dO, scale=None, ds=None):
+    """The composed path's backward.  Returns fp32 (dq, dk, dv)."""
+    B, S, H, Hkv, hd = _dims(q, k)
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    for t, n, shp in ((q, "q", (B, H, S, hd)), (k, "k", (B, Hkv, S, hd)), (v, "v", (B, Hkv, S, hd)),
+                      (dO, "dO", (B, H, S, hd))):
+        _check_tensor(t, n, shp, q.dtype)
+    _check_tensor(p, "p", (B, H, S, S), torch.float32)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    ds = torch.empty((B, H, S, S), **f32) if ds is None else ds
+    _check_tensor(ds, "ds", (B, H, S, S), torch.float32)
+    dq = torch.empty((B, H, S, hd), **f32)
+    dk = torch.empty((B, Hkv, S, hd), **f32)
+    dv = torch.empty((B, Hkv, S, hd), **f32)
+    check(lib().xattn_composed_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), p.data_ptr(),
+                                   p.numel() * 4, dO.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), ds.data_ptr(), ds.numel() * 4, B, S, H, Hkv, hd,
+                                   scale, _code(q), _stream(q)))
+    return dq, dk, dv

@@ -264,6 +264,43 @@ int xattn_decode(const void* q, const void* k, const void* v, const int* lens, v
   return launch_status();
 }
 
+size_t xattn_composed_buffer_bytes(int B, int S, int H) {
+  if (B <= 0 || S <= 0 || H <= 0) return 0;
+  return sizeof(float) * (size_t)B * (size_t)H * (size_t)S * (size_t)S;
+}
+
+int xattn_composed_fwd(const void* q, const void* k, const void* v, void* o, float* lse, float* p,
+                       size_t p_bytes, int B, int S, int H, int Hkv, int hd, float scale,
+                       int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !p) return XATTN_ERR_NULL;
+  const int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (p_bytes < xattn_composed_buffer_bytes(B, S, H)) return XATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(p))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_composed_fwd(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, o, lse, p, scale,
+                             static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+int xattn_composed_bwd(const void* q, const void* k, const void* v, const float* p,
+                       size_t p_bytes, const void* dO, float* dq, float* dk, float* dv, float* ds,
+                       size_t ds_bytes, int B, int S, int H, int Hkv, int hd, float scale,
+                       int dtype, void* stream) {
+  if (!q || !k || !v || !p || !dO || !dq || !dk || !dv || !ds) return XATTN_ERR_NULL;
+  const int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  const size_t need = xattn_composed_buffer_bytes(B, S, H);
+  if (p_bytes < need || ds_bytes < need) return XATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(p) || !aligned16(dO) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ds))
+    return XATTN_ERR_ALIGN;
+  xattn::launch_composed_bwd(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, p, dO, dq, dk, dv, ds,
+                             scale, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 const char* xattn_strerror(int status) {
   switch (status) {
     case XATTN_OK: return "success";

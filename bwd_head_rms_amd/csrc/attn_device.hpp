@@ -347,7 +347,6 @@ __device__ __forceinline__ f32x16 zero_acc() {
   return z;
 }
 
-// Store four consecutive fp32 values (d0 .. d0+3 of one row) as T.
 // Valid length of sequence b of a right-padded batch: lens[b] clamped to
 // [0, S], or S when there are no lengths.
 __device__ __forceinline__ int seq_len(const int* lens, int b, int S) {
@@ -363,6 +362,7 @@ __device__ __forceinline__ void zero_row(float* row) {
   for (int d = 0; d < HD; d += 4) *reinterpret_cast<float4*>(row + d) = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Store four consecutive fp32 values (d0 .. d0+3 of one row) as T.
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d);
 

@@ -47,6 +47,14 @@ void launch_qknorm_rope_bwd(int dtype, const NormDims& d, const void* x, const f
                             const float* dout, float* dx, float* dw, float* ws, float eps,
                             float base, hipStream_t stream);
 
+// Composed path: scores, causal softmax and products through S x S fp32
+// buffers p (probabilities, kept from forward to backward) and ds ([B][H][S][S]).
+void launch_composed_fwd(int dtype, const Dims& d, const void* q, const void* k, const void* v,
+                         void* o, float* lse, float* p, float scale, hipStream_t stream);
+void launch_composed_bwd(int dtype, const Dims& d, const void* q, const void* k, const void* v,
+                         const float* p, const void* dO, float* dq, float* dk, float* dv,
+                         float* ds, float scale, hipStream_t stream);
+
 // Decode attention: q, o [B][H][hd]; k, v [B][Hkv][T][hd] with T in Dims::S;
 // lens [B] (nullable); part is the workspace (nullable when part_bytes == 0).
 struct DecodePlan {

@@ -210,6 +210,34 @@ int xattn_bwd_ragged(const void* q, const void* k, const void* v, const void* o,
                      size_t workspace_bytes, void* stream);
 
 /*
+ * The composed path: the same operation as xattn_fwd / xattn_bwd computed the
+ * way the batched path of the KI-1 fix on "xtrain -- Known Issues & Perf
+ * Backlog" does it (a batched Q.K^T, a causal softmax, then P.V, through an
+ * S x S buffer per (batch, head); the fused kernel of row T14 of the "xtrain
+ * evolution overview" infra table replaces it).  For comparing the two paths.
+ *
+ *   p   [B][H][S][S] float: forward output, backward input -- the causal
+ *       probabilities P_ij (j <= i) in its lower triangle; entries past the
+ *       diagonal up to the end of the row's 128-column tile are 0, the rest
+ *       unspecified.  This buffer is the path's memory cost.
+ *   ds  [B][H][S][S] float: backward scratch (dP, then dS), contents on entry
+ *       irrelevant.
+ * Both must hold at least xattn_composed_buffer_bytes(B, S, H) bytes (the
+ * sizes are passed), 16-byte aligned.  Other arguments, layouts, dtypes and
+ * rounding points as xattn_fwd / xattn_bwd.  Returns an xattn_status.
+ */
+size_t xattn_composed_buffer_bytes(int B, int S, int H);
+
+int xattn_composed_fwd(const void* q, const void* k, const void* v, void* o, float* lse, float* p,
+                       size_t p_bytes, int B, int S, int H, int Hkv, int hd, float scale,
+                       int dtype, void* stream);
+
+int xattn_composed_bwd(const void* q, const void* k, const void* v, const float* p,
+                       size_t p_bytes, const void* dO, float* dq, float* dk, float* dv, float* ds,
+                       size_t ds_bytes, int B, int S, int H, int Hkv, int hd, float scale,
+                       int dtype, void* stream);
+
+/*
  * Decode attention: the new query of each sequence against that sequence's
  * key/value cache (the decode-attention primitive of the "xtrain evolution
  * overview" page, post-training stage: milestone M2a -- one query against the

@@ -278,3 +278,45 @@ def test_fwd_ragged_rejects(L, kw, status):
     (dict(dk=P + 4), ALIGN), (dict(hd=128), HEAD_DIM)])
 def test_bwd_ragged_rejects(L, kw, status):
     assert rbwd(L, **kw) == status
+
+
+# -- composed path ------------------------------------------------------------------
+def cfwd(L, p_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, p=P, B=1, S=16, H=2, Hkv=2, hd=16, scale=0.25, dtype=0)
+    a.update(kw)
+    if p_bytes is None:
+        p_bytes = L.xattn_composed_buffer_bytes(a["B"], a["S"], a["H"])
+    return L.xattn_composed_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["p"], p_bytes, a["B"],
+                                a["S"], a["H"], a["Hkv"], a["hd"], a["scale"], a["dtype"], None)
+
+
+def cbwd(L, p_bytes=None, ds_bytes=None, **kw):
+    a = dict(q=P, k=P, v=P, p=P, dO=P, dq=P, dk=P, dv=P, ds=P, B=1, S=16, H=2, Hkv=2, hd=16,
+             scale=0.25, dtype=0)
+    a.update(kw)
+    need = L.xattn_composed_buffer_bytes(a["B"], a["S"], a["H"])
+    return L.xattn_composed_bwd(a["q"], a["k"], a["v"], a["p"], need if p_bytes is None else p_bytes,
+                                a["dO"], a["dq"], a["dk"], a["dv"], a["ds"],
+                                need if ds_bytes is None else ds_bytes, a["B"], a["S"], a["H"],
+                                a["Hkv"], a["hd"], a["scale"], a["dtype"], None)
+
+
+def test_composed_buffer_bytes(L):
+    assert L.xattn_composed_buffer_bytes(4, 2048, 16) == 4 * 4 * 16 * 2048 * 2048  # 1.07 GB
+    assert L.xattn_composed_buffer_bytes(0, 16, 2) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=None), NULL), (dict(lse=None), NULL), (dict(S=0), SHAPE), (dict(H=3, Hkv=2), GQA),
+    (dict(hd=8), HEAD_DIM), (dict(dtype=5), DTYPE), (dict(scale=float("inf")), SCALE),
+    (dict(p_bytes=16), WORKSPACE), (dict(p=P + 4), ALIGN), (dict(q=P + 2), ALIGN)])
+def test_composed_fwd_rejects(L, kw, status):
+    assert cfwd(L, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ds=None), NULL), (dict(dO=None), NULL), (dict(p_bytes=0), WORKSPACE),
+    (dict(ds_bytes=100), WORKSPACE), (dict(ds=P + 8), ALIGN), (dict(dk=P + 4), ALIGN),
+    (dict(B=-1), SHAPE)])
+def test_composed_bwd_rejects(L, kw, status):
+    assert cbwd(L, **kw) == status
