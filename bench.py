@@ -55,9 +55,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "f53c24f3649cf9c8", "read": 90.48e6, "write": 67.61e6},
-    "dq": {"src": "49b93af81961c064", "read": 149.24e6, "write": 34.71e6},
-    "fwd": {"src": "c29bcd8c4f573880", "read": 61.91e6, "write": 17.30e6},
+    "dkdv": {"src": "af184119d0789e9e", "read": 86.07e6, "write": 67.15e6},
+    "dq": {"src": "b7170ac06f5c1ca0", "read": 170.76e6, "write": 34.63e6},
+    "fwd": {"src": "e603a112aa76b343", "read": 56.12e6, "write": 20.45e6},
 }
 
 
