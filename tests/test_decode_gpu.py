@@ -9,8 +9,9 @@ equals the last row of causal attention there), every head dimension and dtype,
 GQA groups that take each heads-per-workgroup variant (1, 2, 4, 8 and two passes
 of 8), caches of one chunk and of many (the split and merge path), ragged
 lengths on chunk boundaries with NaN beyond each length (never read), empty
-sequences, and the full-size cache the benchmark times on sampled rows.  The
-result is also checked bitwise run to run.
+sequences, the full-size cache the benchmark times on sampled rows, and the
+longest cache accepted (4096 chunks).  The result is also checked bitwise run
+to run.
 """
 import numpy as np
 import pytest
@@ -116,3 +117,18 @@ def test_bitwise_run_to_run():
     o1, l1 = _gpu(a, "bf16")
     o2, l2 = _gpu(a, "bf16")
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_longest_cache():
+    """The longest cache decode accepts (4194304 positions: 4096 chunks of 1024,
+    the merge kernel's limit), hd 16 bf16, one sequence; a shorter length on a
+    second sequence exercises a partly filled chunk list."""
+    T = 1 << 22
+    B, H, Hkv, hd = 2, 2, 1, 16
+    rng = np.random.default_rng(2024)
+    a = {"q": rng.standard_normal((B, H, hd), dtype=np.float32),
+         "k": rng.standard_normal((B, Hkv, T, hd), dtype=np.float32),
+         "v": rng.standard_normal((B, Hkv, T, hd), dtype=np.float32)}
+    a = {n: inputs.bf16_round(x) for n, x in a.items()}
+    Hh.log(f"decode longest cache T={T}")
+    _check(a, "bf16", "T=2^22", lens=[T, 3 * T // 4 + 5])
