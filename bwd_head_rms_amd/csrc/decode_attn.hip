@@ -25,7 +25,8 @@
 //     (unnormalised sum, max, weight sum) and a second kernel merges the chunks
 //     in ascending order.  Fixed orders throughout: results are bitwise
 //     reproducible run to run.
-// Scores are kept in base-2 units (q is pre-multiplied by scale * log2 e).
+// Scores are kept in base-2 units (multiplied by scale * log2 e); bf16 scores
+// use v_dot2_f32_bf16 on the packed query and key pieces.
 #include "attn_device.hpp"
 #include "launch.hpp"
 
@@ -133,12 +134,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
     return;
   }
 
-  float qv[GC][EPL];
+  // the query piece: bf16 stays packed (its products with bf16 keys are exact
+  // in fp32 and go through v_dot2_f32_bf16, scaled after the sum); fp32 is
+  // pre-scaled by scale * log2 e
+  float qv[GC][sizeof(T) == 2 ? 1 : EPL];
+  uint4 qraw[GC];
 #pragma unroll
   for (int t = 0; t < GC; ++t) {
-    load_piece<T>(q + (size_t)(b * H + h0 + t) * HD + piece * EPL, qv[t]);
+    qraw[t] = load_raw(q + (size_t)(b * H + h0 + t) * HD + piece * EPL);
+    if constexpr (sizeof(T) == 4) {
+      widen<T>(qraw[t], qv[t]);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[t][e] *= scale_log2;
+      for (int e = 0; e < EPL; ++e) qv[t][e] *= scale_log2;
+    }
   }
 
   const size_t plane = ((size_t)b * Hkv + g) * (size_t)Tc * HD;
@@ -167,18 +175,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
       const int r = r0 + u;
       const int jj = r * KPR + wave * KPW + slot;  // position within the chunk
       const bool live = j0 + jj < j1;
-      float kv[EPL];
-      widen<T>(buf[u], kv);
+      float sv[GC];
+      if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, buf[u]);
+#pragma unroll
+        for (int t = 0; t < GC; ++t) {
+          const bf16x8 qb = __builtin_bit_cast(bf16x8, qraw[t]);
+          float a = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            a = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{qb[e], qb[e + 1]}, bf16x2{kb[e], kb[e + 1]}, a,
+                                                false);
+          sv[t] = a * scale_log2;
+        }
+      } else {
+        float kv[EPL];
+        widen<T>(buf[u], kv);
+#pragma unroll
+        for (int t = 0; t < GC; ++t) {
+          float acc1 = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc1 += qv[t][e] * kv[e];
+          sv[t] = acc1;
+        }
+      }
       // refill (past the last round: the chunk's last row again, a cache hit)
       buf[u] = load_raw(kp + row_of(r + U < rounds ? r + U : rounds - 1));
-      float sv[GC];
-#pragma unroll
-      for (int t = 0; t < GC; ++t) {
-        float acc1 = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc1 += qv[t][e] * kv[e];
-        sv[t] = acc1;
-      }
 #pragma unroll
       for (int off = 1; off < TPK; off *= 2) {
 #pragma unroll
