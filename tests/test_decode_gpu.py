@@ -132,3 +132,13 @@ def test_longest_cache():
     a = {n: inputs.bf16_round(x) for n, x in a.items()}
     Hh.log(f"decode longest cache T={T}")
     _check(a, "bf16", "T=2^22", lens=[T, 3 * T // 4 + 5])
+
+
+def test_lengths_are_clamped():
+    """Lengths past the capacity act as T, negative ones as 0 (empty)."""
+    T = 600
+    a = _rand(3, T, 4, 2, 32, "f32", seed=12)
+    o, lse = _gpu(a, "f32", lens=[T + 77, -3, 250])
+    o_ref, lse_ref = _gpu(a, "f32", lens=[T, 0, 250])
+    assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+    _check(a, "f32", "clamped lengths", lens=[T, 0, 250])
