@@ -82,7 +82,7 @@ int bwd_dq_impl(const void* q, const void* k, const void* v, const void* o, cons
 
 int bwd_dkdv_impl(const void* q, const void* k, const void* v, const float* lse, const void* dO,
                   const int* lens, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
-                  float scale, int dtype, const void* workspace, size_t workspace_bytes,
+                  float scale, int dtype, void* workspace, size_t workspace_bytes,
                   void* stream) {
   if (!q || !k || !v || !lse || !dO || !dk || !dv) return XATTN_ERR_NULL;
   const int rc = check_bwd_common(B, S, H, Hkv, hd, scale, dtype, workspace, workspace_bytes);
@@ -91,7 +91,7 @@ int bwd_dkdv_impl(const void* q, const void* k, const void* v, const float* lse,
       !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) || !aligned4(lens))
     return XATTN_ERR_ALIGN;
   xattn::launch_bwd_dkdv(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, lse, dO,
-                         static_cast<const float*>(workspace), dk, dv, lens, scale,
+                         static_cast<float*>(workspace), dk, dv, lens, scale,
                          static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -124,7 +124,12 @@ int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, 
 size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype) {
   if (dtype != XATTN_F32 && dtype != XATTN_BF16) return 0;
   if (check_shape(B, S, H, Hkv, hd) != XATTN_OK) return 0;
-  return 2 * sizeof(float) * (size_t)B * (size_t)H * (size_t)S;  // D and LSE*log2e per row
+  const xattn::Dims d{B, S, H, Hkv, hd};
+  const int R = xattn::dkdv_split(d, dtype);
+  if (R == 1) return 2 * sizeof(float) * (size_t)B * (size_t)H * (size_t)S;  // D and LSE*log2e
+  // plus the partial dk, dv of a group split over workgroups
+  return sizeof(float) * (xattn::dkdv_part_offset(d) +
+                          2 * (size_t)R * (size_t)B * (size_t)Hkv * (size_t)S * (size_t)hd);
 }
 
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -136,7 +141,7 @@ int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, con
 
 int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                    const void* dO, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
-                   float scale, int dtype, const void* workspace, size_t workspace_bytes,
+                   float scale, int dtype, void* workspace, size_t workspace_bytes,
                    void* stream) {
   return bwd_dkdv_impl(q, k, v, lse, dO, nullptr, dk, dv, B, S, H, Hkv, hd, scale, dtype,
                        workspace, workspace_bytes, stream);

@@ -40,8 +40,9 @@ template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ dws,
-    float* __restrict__ dk, float* __restrict__ dv, const int* __restrict__ lens, int B, int S,
-    int H, int Hkv, int nkt, int BG, float c, float scale) {
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ part,
+    const int* __restrict__ lens, int B, int S, int H, int Hkv, int nkt, int BG, int R, float c,
+    float scale) {
   using C = DkvCfg<T, HD>;
   using M = Mma<T>;
   __shared__ __align__(16) T sQ[2][C::TILE];
@@ -52,17 +53,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 31, g = lane >> 5;
   const int bid = blockIdx.x;
-  const int kt = bid / BG;  // key tile 0 (the heaviest) first
+  const int kt = bid / (BG * R);  // key tile 0 (the heaviest) first
   const int bg = bid % BG;
+  const int rs = (bid / BG) % R;  // which of the R slices of the group's query heads
   const int b = bg / Hkv, kvh = bg % Hkv;
   const int group = H / Hkv;
   const size_t kvplane = ((size_t)b * Hkv + kvh) * S * HD;
+  // With R > 1 the group is split over R workgroups, each taking H/Hkv/R
+  // consecutive query heads: slice rs writes its partial dK, dV into plane rs
+  // of `part` ([2][R][B][Hkv][S][hd] in the workspace), summed afterwards in
+  // ascending rs by dkdv_group_sum_kernel.
+  const size_t kv_elems = (size_t)B * Hkv * S * HD;
+  float* outk = R > 1 ? part + (size_t)rs * kv_elems : dk;
+  float* outv = R > 1 ? part + (size_t)(R + rs) * kv_elems : dv;
   const int n = seq_len(lens, b, S);  // rows and keys past n are padding
   if (kt * C::BN >= n) {              // a tile of padding keys only: dk = dv = 0
     for (int r = tid; r < C::BN; r += C::NT)
       if (kt * C::BN + r < S) {
-        zero_row<HD>(dk + kvplane + (size_t)(kt * C::BN + r) * HD);
-        zero_row<HD>(dv + kvplane + (size_t)(kt * C::BN + r) * HD);
+        zero_row<HD>(outk + kvplane + (size_t)(kt * C::BN + r) * HD);
+        zero_row<HD>(outv + kvplane + (size_t)(kt * C::BN + r) * HD);
       }
     return;
   }
@@ -96,14 +105,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int qt_first = (kt * C::BN) / C::BMQ;
   const int nq = (n + C::BMQ - 1) / C::BMQ;  // query tiles holding rows of the sequence
   const int per_head = nq - qt_first;
-  const int iters = group * per_head;
+  const int heads = group / R;  // query heads this workgroup sums over
+  const int r_lo = rs * heads;
+  const int iters = heads * per_head;
 
   wait_global_loads();  // the key / value operands above are in registers
   Stager<T, HD, C::BMQ, C::NW> stQ, stO;
   const float* lse2 = dws + (size_t)B * H * S;  // LSE*log2e, written by the dq kernel
   // issue the copies of tile `it` (Q, dO, LSE*log2e, D) into buffer `buf`
   auto issue = [&](int it, int buf) {
-    const int r = it / per_head, qt = qt_first + it % per_head;
+    const int r = r_lo + it / per_head, qt = qt_first + it % per_head;
     const size_t bh = (size_t)b * H + (size_t)kvh * group + r;
     const int row0 = qt * C::BMQ;
     // rows past n (padding, or past S) read zero: their Q, dO, LSE and D are
@@ -285,13 +296,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   if constexpr (sizeof(T) == 2) mma_agpr_drain();
   if (!kv_ok) {  // padding keys inside the sequence's last tile
     if (g == 0 && my_kv < S) {
-      zero_row<HD>(dk + kvplane + (size_t)my_kv * HD);
-      zero_row<HD>(dv + kvplane + (size_t)my_kv * HD);
+      zero_row<HD>(outk + kvplane + (size_t)my_kv * HD);
+      zero_row<HD>(outv + kvplane + (size_t)my_kv * HD);
     }
     return;
   }
-  float* krow = dk + kvplane + (size_t)my_kv * HD;
-  float* vrow = dv + kvplane + (size_t)my_kv * HD;
+  float* krow = outk + kvplane + (size_t)my_kv * HD;
+  float* vrow = outv + kvplane + (size_t)my_kv * HD;
 #pragma unroll
   for (int db = 0; db < C::ND; ++db)
 #pragma unroll
@@ -306,21 +317,73 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     }
 }
 
+constexpr long kDkvSplitBelow = 512;  // kv tiles under which a group is split
+// Workgroups a split aims for.  Each slice adds a partial dK, dV plane to
+// write and re-read; the fp32 kernel spends longer per tile, so it gains from
+// more slices than bf16 loses to the extra traffic.
+constexpr long kDkvSplitTargetF32 = 1024, kDkvSplitTargetBf16 = 512;
+
+// dk = sum over r of part_k[r], dv = sum over r of part_v[r], r ascending
+// (the group sum of a split group), four floats per thread.
+__global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float* __restrict__ part,
+                                                             float* __restrict__ dk,
+                                                             float* __restrict__ dv, long n4,
+                                                             int R) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const bool is_v = i >= n4;
+  const long e = is_v ? i - n4 : i;
+  const float4* src = reinterpret_cast<const float4*>(part) + (is_v ? (long)R * n4 : 0) + e;
+  float4 a = src[0];
+  for (int r = 1; r < R; ++r) {
+    const float4 b = src[(long)r * n4];
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  reinterpret_cast<float4*>(is_v ? dv : dk)[e] = a;
+}
+
+int dkdv_split(const Dims& d, int dtype) {
+  const int group = d.H / d.Hkv;
+  const long tiles = (long)d.B * d.Hkv * ((d.S + 127) / 128);
+  if (group == 1 || tiles >= kDkvSplitBelow) return 1;
+  // fewer workgroups than two per CU: split each group into the fewest slices
+  // (a divisor of the group) that reach the target
+  const long target = dtype == 0 ? kDkvSplitTargetF32 : kDkvSplitTargetBf16;
+  int R = 1;
+  while (R < group && tiles * R < target) {
+    do { ++R; } while (group % R != 0);
+  }
+  return R;
+}
+
+size_t dkdv_part_offset(const Dims& d) {
+  return (2 * (size_t)d.B * d.H * d.S + 3) / 4 * 4;  // floats, keeps 16-byte alignment
+}
+
 template <typename T, int HD>
 static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* v,
-                       const float* lse, const void* dO, const float* dws, float* dk, float* dv,
+                       const float* lse, const void* dO, float* dws, float* dk, float* dv,
                        const int* lens, float scale, hipStream_t stream) {
   using C = DkvCfg<T, HD>;
+  static_assert(C::BN == 128, "dkdv_split assumes 128-key tiles");
   const int nkt = (d.S + C::BN - 1) / C::BN;
   const int BG = d.B * d.Hkv;
-  dim3 grid((unsigned)(nkt * BG)), block(C::NT);
+  const int R = dkdv_split(d, sizeof(T) == 4 ? 0 : 1);
+  // the partials follow the per-row statistics in the workspace
+  float* part = R > 1 ? dws + dkdv_part_offset(d) : nullptr;
+  dim3 grid((unsigned)(nkt * BG * R)), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
-                     (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, lens, d.B, d.S,
-                     d.H, d.Hkv, nkt, BG, scale * kLog2e, scale);
+                     (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, part, lens, d.B,
+                     d.S, d.H, d.Hkv, nkt, BG, R, scale * kLog2e, scale);
+  if (R > 1) {
+    const long n4 = (long)d.B * d.Hkv * d.S * HD / 4;
+    hipLaunchKernelGGL(dkdv_group_sum_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256),
+                       0, stream, (const float*)part, dk, dv, n4, R);
+  }
 }
 
 void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,
-                     const float* lse, const void* dO, const float* dws, float* dk, float* dv,
+                     const float* lse, const void* dO, float* dws, float* dk, float* dv,
                      const int* lens, float scale, hipStream_t stream) {
   if (dtype == 0) {
     if (d.hd == 16) dkdv_typed<float, 16>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);

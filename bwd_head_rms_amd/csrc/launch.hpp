@@ -22,10 +22,16 @@ void launch_bwd_dq(int dtype, const Dims& d, const void* q, const void* k, const
                    const void* o, const float* lse, const void* dO, float* dq, float* dws,
                    const int* lens, float scale, hipStream_t stream);
 
-// Backward, second kernel: dk, dv (group-summed), reading D from `dws`.
+// Backward, second kernel: dk, dv (group-summed), reading D from `dws`.  When
+// dkdv_split(d, dtype) > 1 the query heads of a group are spread over workgroups that
+// write partial dk, dv into `dws` at dkdv_part_offset(d) floats
+// ([2][group][B][Hkv][S][hd]), summed in ascending head order by a second
+// kernel.
 void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,
-                     const float* lse, const void* dO, const float* dws, float* dk, float* dv,
+                     const float* lse, const void* dO, float* dws, float* dk, float* dv,
                      const int* lens, float scale, hipStream_t stream);
+int dkdv_split(const Dims& d, int dtype);
+size_t dkdv_part_offset(const Dims& d);
 
 // Per-head RMS QK-norm + rotary embedding.  x [B][S][H][hd] (token-major),
 // out and dout [B][H][S][hd], dx [B][S][H][hd], w and dw [hd].

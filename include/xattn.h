@@ -94,7 +94,13 @@ int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace xattn_bwd needs: 8*B*H*S (two floats per query
- * row: -D = -rowsum(dO * o) and LSE * log2(e)), O(B*H*S), never S x S.
+ * row: -D = -rowsum(dO * o) and LSE * log2(e)), O(B*H*S), never S x S.  For
+ * grouped-query shapes with few kv tiles (B * Hkv * ceil(S/128) < 512) the
+ * dk/dv kernel splits the query heads of each group into R slices (R the
+ * least divisor of H/Hkv with R * B * Hkv * ceil(S/128) >= 1024 for fp32,
+ * >= 512 for bf16, else H/Hkv), one workgroup each, and keeps their partial
+ * dk, dv here too: the first part rounded up to a multiple of 16 bytes, plus
+ * 8 * R * B * Hkv * S * hd bytes.
  * Returns 0 for invalid shapes.
  */
 size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype);
@@ -126,7 +132,9 @@ int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
  *   -D = -rowsum(dO * o) and LSE * log2(e) in the workspace ([2][B][H][S] float).
  * xattn_bwd_dkdv: writes dk, dv [B][Hkv][S][hd] float; reads both per-row
  *   values from the workspace (not lse), so it must be ordered after an
- *   xattn_bwd_dq call with the same q, o, dO, lse, shapes and workspace.
+ *   xattn_bwd_dq call with the same q, o, dO, lse, shapes and workspace; on
+ *   grouped-query shapes it also writes partial sums past them (see
+ *   xattn_bwd_workspace_bytes).
  * Argument meaning, layout, validation and status codes are those of xattn_bwd.
  */
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -135,7 +143,7 @@ int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, con
 
 int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                    const void* dO, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
-                   float scale, int dtype, const void* workspace, size_t workspace_bytes,
+                   float scale, int dtype, void* workspace, size_t workspace_bytes,
                    void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

@@ -98,11 +98,29 @@ def test_bad_scale(L, scale):
 
 def test_workspace_size_and_checks(L):
     assert L.xattn_bwd_workspace_bytes(4, 2048, 16, 16, 64, 1) == 8 * 4 * 16 * 2048
-    assert L.xattn_bwd_workspace_bytes(16, 1024, 8, 2, 64, 0) == 8 * 16 * 8 * 1024
+    # GQA with 16*2*8 = 256 kv tiles: the dk/dv kernel splits each group of 4
+    # query heads over workgroups (4 slices for fp32, 2 for bf16) and keeps
+    # partial dk, dv in the workspace
+    assert L.xattn_bwd_workspace_bytes(16, 1024, 8, 2, 64, 0) == (
+        8 * 16 * 8 * 1024 + 2 * 4 * (4 * 16 * 2 * 1024 * 64))
+    assert L.xattn_bwd_workspace_bytes(16, 1024, 8, 2, 64, 1) == (
+        8 * 16 * 8 * 1024 + 2 * 4 * (2 * 16 * 2 * 1024 * 64))
+    # a group of 6 over 256 tiles in bf16: 2 slices; over 100 tiles: 6 (no divisor 5)
+    assert L.xattn_bwd_workspace_bytes(16, 1024, 12, 2, 16, 1) == (
+        8 * 16 * 12 * 1024 + 2 * 4 * (2 * 16 * 2 * 1024 * 16))
+    assert L.xattn_bwd_workspace_bytes(25, 512, 6, 1, 16, 1) == (
+        8 * 25 * 6 * 512 + 2 * 4 * (6 * 25 * 512 * 16))
+    # odd row count: the partials start on the next 16-byte boundary
+    assert L.xattn_bwd_workspace_bytes(1, 3, 3, 1, 16, 1) == 4 * 20 + 2 * 4 * (3 * 3 * 16)
+    # enough kv tiles (4*2*64 = 512): no split
+    assert L.xattn_bwd_workspace_bytes(4, 8192, 8, 2, 64, 1) == 8 * 4 * 8 * 8192
     assert L.xattn_bwd_workspace_bytes(1, 16, 3, 2, 16, 0) == 0  # invalid GQA shape
     assert L.xattn_bwd_workspace_bytes(1, 16, 2, 2, 16, 9) == 0  # invalid dtype
     assert bwd(L, ws=None) == WORKSPACE
     assert bwd(L, ws_bytes=8 * 2 * 16 - 1) == WORKSPACE
+    # a GQA split shape needs room for the partials too
+    assert bwd(L, H=4, Hkv=2) == WORKSPACE
+    assert bwd(L, H=4, Hkv=2, ws_bytes=L.xattn_bwd_workspace_bytes(1, 16, 4, 2, 16, 0) - 4) == WORKSPACE
 
 
 def test_size_limits(L):

@@ -66,6 +66,15 @@ def test_gqa_equals_repeated_mha(dtype):
         summed = sum(mha[n][:, [g * group + r for g in range(Hkv)]] for r in range(group))
         err = np.max(np.abs(gqa[n] - summed))
         assert err <= 1e-5 * np.max(np.abs(summed)), f"GQA {n} != group sum of MHA ({err})"
+        # this shape has few kv tiles, so each query head of a group takes its
+        # own workgroup: the partials are the MHA heads' gradients bit for bit
+        # and the group sum adds them in fp32 in ascending head order
+        heads = [mha[n][:, [g * group + r for g in range(Hkv)]].astype(np.float32)
+                 for r in range(group)]
+        exact = heads[0]
+        for x in heads[1:]:
+            exact = exact + x
+        assert np.array_equal(gqa[n].astype(np.float32), exact), f"GQA {n}: split sum order"
 
 
 def test_group_one_is_mha_bitwise():
@@ -157,7 +166,9 @@ def test_outputs_fully_overwritten():
     o2 = fill(torch.empty_like(o1))
     l2 = fill(torch.empty_like(l1))
     api.fwd(t["q"], t["k"], t["v"], o=o2, lse=l2)
-    ws = fill(torch.empty(2 * 1 * 2 * 130, dtype=torch.float32, device="cuda"))
+    # a group of 2 over few kv tiles: the workspace also holds partial dk, dv
+    ws = fill(torch.empty(api.workspace_bytes(1, 130, 2, 1, 64, 1) // 4, dtype=torch.float32,
+                          device="cuda"))
     g2 = [fill(torch.empty_like(x)) for x in g1]
     api.bwd(t["q"], t["k"], t["v"], o1, l1, t["dO"], dq=g2[0], dk=g2[1], dv=g2[2], workspace=ws)
     torch.cuda.synchronize()
