@@ -55,9 +55,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "5056202c65f24869", "read": 84.49e6, "write": 67.27e6},
-    "dq": {"src": "dfedf9d5ec63f028", "read": 143.33e6, "write": 34.62e6},
-    "fwd": {"src": "f1ac0c87ec1aa31b", "read": 56.06e6, "write": 20.45e6},
+    "dkdv": {"src": "48a91cec9f824448", "read": 80.75e6, "write": 67.21e6},
+    "dq": {"src": "121fde45ad57119d", "read": 141.91e6, "write": 34.61e6},
+    "fwd": {"src": "f1ac0c87ec1aa31b", "read": 56.02e6, "write": 20.45e6},
 }
 
 

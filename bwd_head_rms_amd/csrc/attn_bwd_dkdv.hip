@@ -222,11 +222,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
           for (int qb = 0; qb < C::NQB; ++qb) {
             f32x16 s = zero_acc(), dp = dnext;
+            // raised priority while issuing matrix products, so that they queue
+            // on the matrix core while the other wave of the SIMD runs VALU
+            // work (measured: the kernel 3-4% faster)
+            __builtin_amdgcn_s_setprio(2);
 #pragma unroll
             for (int ks = 0; ks < C::NKS; ++ks) {
               M::mma(s, aq[ks], kf[ks]);
               M::mma(dp, ao[ks], vf[ks]);
             }
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
             typename M::frag to[C::NAS][C::ND], tq[C::NAS][C::ND];
 #pragma unroll
@@ -256,6 +261,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
               sf[ks] = acc_frag<T>(dp, ks * M::KPL);
             }
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(2);
 #pragma unroll
             for (int ks = 0; ks < C::NAS; ++ks)
 #pragma unroll
@@ -263,6 +269,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
                 acc_mma(dvacc[db], to[ks][db], pf[ks]);
                 acc_mma(dkacc[db], tq[ks][db], sf[ks]);
               }
+            __builtin_amdgcn_s_setprio(0);
             if (qb + 1 < C::NQB) {
 #pragma unroll
               for (int ks = 0; ks < C::NKS; ++ks) {

@@ -130,11 +130,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
         constexpr bool MASK = decltype(mask_tag)::value;
         const int kb0 = kv_t0 + 32 * cb;
         f32x16 s = zero_acc(), dp = negD;
+        // A wave issuing matrix products runs at raised priority, so that its
+        // products queue on the matrix core while the other waves of the SIMD
+        // run their VALU work (measured: the kernel 5% faster).
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           M::mma(s, row_frag_lds<T, HD, C::BN>(tK, 32 * cb + li, g, ks), qf[ks]);
           M::mma(dp, row_frag_lds<T, HD, C::BN>(tV, 32 * cb + li, g, ks), df[ks]);
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(fmaf(s[r], c, -lse2));
@@ -144,6 +149,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
           }
           s[r] = p * dp[r];  // dS^T = P (dP - D)
         }
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < C::NAS; ++ks) {
           const typename M::frag sf = acc_frag<T>(s, ks * M::KPL);
@@ -152,6 +158,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
             M::mma(acc[db], accrow_frag<T, HD, C::BN>(tK, 32 * cb, ks, 32 * db, lane), sf);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       };
 
 #pragma unroll
