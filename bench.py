@@ -55,9 +55,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "48a91cec9f824448", "read": 80.75e6, "write": 67.21e6},
-    "dq": {"src": "121fde45ad57119d", "read": 141.91e6, "write": 34.61e6},
-    "fwd": {"src": "f1ac0c87ec1aa31b", "read": 56.02e6, "write": 20.45e6},
+    "dkdv": {"src": "0d51a3ac94cc8ca6", "read": 84.68e6, "write": 67.21e6},
+    "dq": {"src": "802b8bef6e740f9d", "read": 109.77e6, "write": 34.61e6},
+    "fwd": {"src": "f1ac0c87ec1aa31b", "read": 55.77e6, "write": 20.45e6},
 }
 
 

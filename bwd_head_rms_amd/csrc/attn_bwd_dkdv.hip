@@ -36,8 +36,14 @@ struct DkvCfg {
   static constexpr int TILE = Tile<T, HD, BMQ>::ELEMS;
 };
 
+// bf16 keeps the long-lived dK/dV sums in AGPRs at hd 64 (two waves per SIMD
+// either way); at hd 32 they stay in VGPRs so that the kernel fits three waves
+// per SIMD (168 registers) without the compiler's even VGPR/AGPR split.
+template <int HD>
+constexpr bool kDkvAgpr = HD == 64;
+
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 3 : 1))) void attn_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ dws,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ part,
@@ -81,27 +87,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const bool kv_ok = my_kv < n;
   const bool wave_live = kv0 < n;
 
-  typename M::frag kf[C::NKS], vf[C::NKS];
-#pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-    kf[ks] = kv_ok ? row_frag_global<T, HD>(k + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
-    vf[ks] = kv_ok ? row_frag_global<T, HD>(v + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
-  }
-
-  // dK^T / dV^T accumulators live for the whole kernel: bf16 keeps them in AGPRs
-  f32x16 dkacc[C::ND], dvacc[C::ND];
-#pragma unroll
-  for (int d = 0; d < C::ND; ++d) {
-    dkacc[d] = zero_acc();
-    dvacc[d] = zero_acc();
-  }
-  auto acc_mma = [](f32x16& acc, const typename M::frag& a, const typename M::frag& b) {
-    if constexpr (sizeof(T) == 2)
-      mma_agpr(acc, a, b);
-    else
-      M::mma(acc, a, b);
-  };
-
   const int qt_first = (kt * C::BN) / C::BMQ;
   const int nq = (n + C::BMQ - 1) / C::BMQ;  // query tiles holding rows of the sequence
   const int per_head = nq - qt_first;
@@ -109,7 +94,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int r_lo = rs * heads;
   const int iters = heads * per_head;
 
-  wait_global_loads();  // the key / value operands above are in registers
   Stager<T, HD, C::BMQ, C::NW> stQ, stO;
   const float* lse2 = dws + (size_t)B * H * S;  // LSE*log2e, written by the dq kernel
   // issue the copies of tile `it` (Q, dO, LSE*log2e, D) into buffer `buf`
@@ -139,8 +123,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     stQ.commit(sQ[buf], tid);
     stO.commit(sO[buf], tid);
   };
-  issue(0, 0);
-  commit(0);
+  // bf16: the first tile's copies into LDS go out before the key / value
+  // loads, so the two fetches overlap (fp32 stages through registers and
+  // copies after them)
+  if constexpr (sizeof(T) == 2) issue(0, 0);
+  typename M::frag kf[C::NKS], vf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    kf[ks] = kv_ok ? row_frag_global<T, HD>(k + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
+    vf[ks] = kv_ok ? row_frag_global<T, HD>(v + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
+  }
+
+  // dK^T / dV^T accumulators live for the whole kernel: bf16 keeps them in AGPRs
+  f32x16 dkacc[C::ND], dvacc[C::ND];
+#pragma unroll
+  for (int d = 0; d < C::ND; ++d) {
+    dkacc[d] = zero_acc();
+    dvacc[d] = zero_acc();
+  }
+  auto acc_mma = [](f32x16& acc, const typename M::frag& a, const typename M::frag& b) {
+    if constexpr (sizeof(T) == 2 && kDkvAgpr<HD>)
+      mma_agpr(acc, a, b);
+    else
+      M::mma(acc, a, b);
+  };
+
+  if constexpr (sizeof(T) == 4) issue(0, 0);
+  commit(0);  // waits for every load above
   __syncthreads();
 
   for (int it = 0; it < iters; ++it) {
@@ -300,7 +309,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     __syncthreads();
   }
 
-  if constexpr (sizeof(T) == 2) mma_agpr_drain();
+  if constexpr (sizeof(T) == 2 && kDkvAgpr<HD>) mma_agpr_drain();
   if (!kv_ok) {  // padding keys inside the sequence's last tile
     if (g == 0 && my_kv < S) {
       zero_row<HD>(outk + kvplane + (size_t)my_kv * HD);

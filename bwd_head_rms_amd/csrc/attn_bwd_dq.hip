@@ -66,6 +66,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const bool wave_live = q0 < n;
   const int wave_kv_end = min(n, q0 + 32);
 
+  // bf16: the first key / value tile's copies into LDS go out before the
+  // per-row loads, so the two fetches overlap (fp32 stages through registers
+  // and copies after them)
+  Stager<T, HD, C::BN, C::NW> stK, stV;
+  if constexpr (sizeof(T) == 2) {
+    stK.issue(kp, 0, n, sK[0], wave, lane, tid);
+    stV.issue(vp, 0, n, sV[0], wave, lane, tid);
+  }
+
   typename M::frag qf[C::NKS], df[C::NKS];
   float Dp = 0.f;
 #pragma unroll
@@ -103,10 +112,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int kv_end = min(n, qt * C::BM + C::BM);
   const int ntiles = (kv_end + C::BN - 1) / C::BN;
 
-  wait_global_loads();  // the per-row operands above are in registers
-  Stager<T, HD, C::BN, C::NW> stK, stV;
-  stK.issue(kp, 0, n, sK[0], wave, lane, tid);
-  stV.issue(vp, 0, n, sV[0], wave, lane, tid);
+  if constexpr (sizeof(T) == 4) {
+    wait_global_loads();  // the per-row operands above are in registers
+    stK.issue(kp, 0, n, sK[0], wave, lane, tid);
+    stV.issue(vp, 0, n, sV[0], wave, lane, tid);
+  }
   wait_global_loads();
   stK.commit(sK[0], tid);
   stV.commit(sV[0], tid);
