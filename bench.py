@@ -5,9 +5,10 @@ long-context workload (B4, S2048, 16 heads of 64, bf16 in / fp32 accumulate):
 xattn_fwd, then the backward as its two kernels (xattn_bwd_dq, xattn_bwd_dkdv,
 which together are exactly xattn_bwd), all through the C ABI on torch's current
 stream with inputs resident in HBM.  W untimed warmup steps, then K timed steps
-between synchronisations.  HIP events between the kernels give each kernel's
-average duration inside the timed region; the dominant kernel's roofline is
-reported against MI355X's dense bf16 MFMA peak.
+between synchronisations.  HIP events between the kernels (timing-only events
+without a system-scope fence, so no cache flush separates the kernels) give
+each kernel's average duration inside the timed region; the dominant kernel's
+roofline is reported against MI355X's dense bf16 MFMA peak.
 
 Counted FLOPs (the FlashAttention-2 convention, causal half only):
     fwd 4*hd*nnz, bwd 10*hd*nnz per (batch, head), nnz = S(S+1)/2
@@ -55,9 +56,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "0d51a3ac94cc8ca6", "read": 84.68e6, "write": 67.21e6},
-    "dq": {"src": "802b8bef6e740f9d", "read": 109.77e6, "write": 34.61e6},
-    "fwd": {"src": "f1ac0c87ec1aa31b", "read": 55.77e6, "write": 20.45e6},
+    "dkdv": {"src": "0d51a3ac94cc8ca6", "read": 82.77e6, "write": 67.19e6},
+    "dq": {"src": "802b8bef6e740f9d", "read": 115.16e6, "write": 34.61e6},
+    "fwd": {"src": "f1ac0c87ec1aa31b", "read": 55.74e6, "write": 20.45e6},
 }
 
 
@@ -83,6 +84,70 @@ def measured_traffic(kernel, workload):
     if workload != inputs.LONG_CONTEXT or not m or m["src"] != kernel_source_hash(kernel):
         return None
     return m["read"] + m["write"]
+
+
+class TimingEvents:
+    """HIP events used only for timing, created with hipEventDisableSystemFence
+    through the HIP runtime that torch has loaded in this process.  An ordinary
+    timing event performs a system-scope fence when it is recorded: a cache
+    write-back and invalidation between the kernels it separates, so every
+    kernel after one would start with a cold L2 and the step would run slower
+    than back-to-back kernels do.  Elapsed times are read after a device
+    synchronisation, which orders the host after the recorded work."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        with open("/proc/self/maps") as fh:
+            paths = [line.split()[-1] for line in fh if "libamdhip64" in line]
+        if not paths:
+            raise RuntimeError("the HIP runtime is not loaded in this process")
+        self._ct = ctypes
+        self._hip = ctypes.CDLL(paths[0])
+        self._made = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def new(self):
+        e = self._ct.c_void_p()
+        self._check(self._hip.hipEventCreateWithFlags(self._ct.byref(e),
+                                                      self._ct.c_uint(self.DISABLE_SYSTEM_FENCE)),
+                    "hipEventCreateWithFlags")
+        self._made.append(e)
+        return e
+
+    def record(self, e, stream_handle):
+        self._check(self._hip.hipEventRecord(e, self._ct.c_void_p(stream_handle)), "hipEventRecord")
+
+    def ms(self, a, b):
+        f = self._ct.c_float()
+        self._check(self._hip.hipEventElapsedTime(self._ct.byref(f), a, b), "hipEventElapsedTime")
+        return f.value
+
+    def close(self):
+        for e in self._made:
+            self._hip.hipEventDestroy(e)
+        self._made = []
+
+
+def time_loop(fn, steps):
+    """Milliseconds per call of `fn` over `steps` back-to-back calls on torch's
+    current stream, between two timing events (after a synchronisation)."""
+    import torch
+    T = TimingEvents()
+    sh = torch.cuda.current_stream().cuda_stream
+    e0, e1 = T.new(), T.new()
+    torch.cuda.synchronize()
+    T.record(e0, sh)
+    for _ in range(steps):
+        fn()
+    T.record(e1, sh)
+    torch.cuda.synchronize()
+    ms = T.ms(e0, e1) / steps
+    T.close()
+    return ms
 
 
 def counted_flops(w):
@@ -132,25 +197,27 @@ def run_gpu(w, steps, warmup):
         fwd(); bwd_dq(); bwd_dkdv()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    T = TimingEvents()
+    ev = [[T.new() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        ev[i][0].record(stream)
+        T.record(ev[i][0], sh)
         fwd()
-        ev[i][1].record(stream)
+        T.record(ev[i][1], sh)
         bwd_dq()
-        ev[i][2].record(stream)
+        T.record(ev[i][2], sh)
         bwd_dkdv()
-        ev[i][3].record(stream)
+        T.record(ev[i][3], sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = ev[0][0].elapsed_time(ev[-1][3])
+    total_ms = T.ms(ev[0][0], ev[-1][3])
     per = {"fwd": [], "dq": [], "dkdv": []}
     for e in ev:
-        per["fwd"].append(e[0].elapsed_time(e[1]))
-        per["dq"].append(e[1].elapsed_time(e[2]))
-        per["dkdv"].append(e[2].elapsed_time(e[3]))
+        per["fwd"].append(T.ms(e[0], e[1]))
+        per["dq"].append(T.ms(e[1], e[2]))
+        per["dkdv"].append(T.ms(e[2], e[3]))
+    T.close()
     avg = {k: float(np.mean(v)) for k, v in per.items()}
     return {"ms_per_step": total_ms / steps, "wall_s": wall, "kernel_ms": avg,
             "device": torch.cuda.get_device_name(dev)}
@@ -201,13 +268,7 @@ def run_norm(w, steps, warmup):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        res[name] = e0.elapsed_time(e1) / steps  # ms
+        res[name] = time_loop(fn, steps)  # ms
     nb = norm_bytes(w)
     roof = {k: {"achieved": round(nb[k] / (res[k] / 1e3) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(nb[k] / (res[k] / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
@@ -290,13 +351,7 @@ def run_decode(wd, steps, warmup):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        call()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_loop(call, steps)
     nb = decode_bytes(wd)
     gbs = nb / (ms / 1e3) / 1e9
     return {"workload": wd.name, "B": wd.B, "T": wd.T, "H": wd.H, "Hkv": wd.Hkv, "hd": wd.hd,
@@ -352,13 +407,7 @@ def run_ragged(rw, steps, warmup):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms[name] = e0.elapsed_time(e1) / steps
+        ms[name] = time_loop(fn, steps)
     flops = sum(14.0 * rw.hd * rw.H * n * (n + 1) / 2 for n in lens)
     tf = flops / (ms["ragged"] / 1e3) / 1e12
     return {"workload": rw.name, "lens": lens, "ms_per_step": round(ms["ragged"], 5),
@@ -410,13 +459,7 @@ def run_composed(w, steps, warmup):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms[name] = e0.elapsed_time(e1) / steps
+        ms[name] = time_loop(fn, steps)
     tot = ms["fwd"] + ms["bwd"]
     tf = counted_flops(w)["total"] / (tot / 1e3) / 1e12
     return {"workload": w.name, "fwd_ms": round(ms["fwd"], 4), "bwd_ms": round(ms["bwd"], 4),
@@ -431,7 +474,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None, help="name from bwd_head_rms_amd.inputs.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
