@@ -296,10 +296,21 @@ def cpu_baseline(w, budget_units=None):
     dt = time.perf_counter() - t0
     nnz = w.S * (w.S + 1) / 2
     flops = 14 * nnz * w.hd * n_units * (w.H // w.Hkv)
+    # the same oracle on one thread, one unit
+    ref.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        ref.run(sub["q"], sub["k"], sub["v"], sub["dO"], scale=w.scale, units=(0, 1))
+        dt1 = time.perf_counter() - t1
+    finally:
+        ref.set_threads(0)
+    flops1 = 14 * nnz * w.hd * (w.H // w.Hkv)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "seconds": dt,
             "sample": f"{n_units} of {w.B * w.Hkv} (batch, kv head) units of {w.name} "
-                      f"({n_units * (w.H // w.Hkv)} heads x S={w.S}, fwd+bwd, fp64)"}
+                      f"({n_units * (w.H // w.Hkv)} heads x S={w.S}, fwd+bwd, fp64)",
+            "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "seconds": dt1, "sample": f"1 unit ({w.H // w.Hkv} heads x S={w.S})"}}
 
 
 def calibrate_copy(nbytes, reps=5):
