@@ -39,6 +39,23 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Position of workgroup `bid` in a heaviest-first list of tiles, rearranged so
+// that the workgroups one CU holds at the same time carry about equal work.  A
+// fresh grid is dealt breadth-first: CU c receives workgroups c, c + ncu,
+// c + 2 ncu, ... (measured on MI355X).  While the first `resident` rounds of ncu
+// workgroups are all in flight together, odd rounds take the list backwards, so
+// a CU that got one of the heaviest tiles in round 0 gets one of the lightest of
+// round 1.  The reversal moves whole blocks of 8, which keeps bid mod 8 (the
+// XCD a workgroup lands on, and with it the head's shared L2).  Later rounds,
+// dispatched as CUs free up, and grids whose CU count is not a multiple of 8,
+// keep the plain order (as does an unknown CU count, ncu <= 0).
+__device__ __forceinline__ int balanced_rank(int bid, int nwg, int ncu, int resident) {
+  if (ncu <= 0 || (ncu & 7) != 0) return bid;
+  const int j = bid / ncu, c = bid % ncu;
+  if ((j & 1) == 0 || j >= resident || (j + 1) * ncu > nwg) return bid;
+  return j * ncu + (ncu - 8 - (c & ~7)) + (c & 7);
+}
+
 // Combine lanes l and l^32 (v_permlane32_swap exchanges the two half-waves: the
 // two results hold x of lanes 0..31 and 32..63 in every lane's position).
 __device__ __forceinline__ float halves_max(float x) {

@@ -21,6 +21,7 @@
 // natural-log LSE = (m + log2 l) * ln 2.  Query head h reads kv head
 // h / (H / Hkv) by address (GQA without a copy, row T15 of the same table).
 // Work order: heaviest query tiles first.
+#include <atomic>
 #include <type_traits>
 
 #include "attn_device.hpp"
@@ -279,7 +280,7 @@ template <int HD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_fwd_pipe_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     bf16* __restrict__ o, float* __restrict__ lse, const int* __restrict__ lens, int S, int H,
-    int Hkv, int nqt, int BH, float c) {
+    int Hkv, int nqt, int BH, int ncu, float c) {
   using P = FwdPipe<HD>;
   using M = Mma<bf16>;
   using frag = M::frag;
@@ -289,7 +290,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int li = lane & 31, g = lane >> 5;
-  const int bid = blockIdx.x;
+  // heaviest tiles first, balanced over the four workgroups a CU holds at once
+  const int bid = balanced_rank(blockIdx.x, gridDim.x, ncu, 4);
   const int qt = nqt - 1 - bid / BH;
   const int bh = bid % BH;
   const int b = bh / H, h = bh % H;
@@ -541,6 +543,21 @@ static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v
                      nqt, BH, scale * kLog2e);
 }
 
+// Compute units of the current device, read once per device.
+static int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return 0;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int HD>
 static void fwd_pipe(const Dims& d, const void* q, const void* k, const void* v, void* o,
                      float* lse, const int* lens, float scale, hipStream_t stream) {
@@ -550,7 +567,7 @@ static void fwd_pipe(const Dims& d, const void* q, const void* k, const void* v,
   dim3 grid((unsigned)(nqt * BH)), block(P::NT);
   hipLaunchKernelGGL((attn_fwd_pipe_kernel<HD>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, lens, d.S,
-                     d.H, d.Hkv, nqt, BH, scale * kLog2e);
+                     d.H, d.Hkv, nqt, BH, device_cu_count(), scale * kLog2e);
 }
 
 void launch_fwd(int dtype, const Dims& d, const void* q, const void* k, const void* v, void* o,
