@@ -98,10 +98,17 @@ class TimingEvents:
 
     def __init__(self):
         import ctypes
+
+        import torch
         with open("/proc/self/maps") as fh:
-            paths = [line.split()[-1] for line in fh if "libamdhip64" in line]
+            paths = sorted({line.split()[-1] for line in fh if "libamdhip64" in line})
         if not paths:
             raise RuntimeError("the HIP runtime is not loaded in this process")
+        if len(paths) > 1:  # use the copy torch runs on
+            torch_lib = os.path.join(os.path.dirname(torch.__file__), "lib")
+            paths = [p for p in paths if os.path.dirname(p) == torch_lib]
+            if len(paths) != 1:
+                raise RuntimeError("cannot tell which HIP runtime torch uses")
         self._ct = ctypes
         self._hip = ctypes.CDLL(paths[0])
         self._made = []
