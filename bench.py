@@ -56,9 +56,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "4ca5eb3cce8b03ae", "read": 84.86e6, "write": 67.14e6},
-    "dq": {"src": "aadd20dd237005da", "read": 109.27e6, "write": 34.60e6},
-    "fwd": {"src": "0145bd59d6ca605b", "read": 55.59e6, "write": 20.45e6},
+    "dkdv": {"src": "1b81d2450cbf39a1", "read": 84.86e6, "write": 67.14e6},
+    "dq": {"src": "2b3aca3ca37b7832", "read": 109.27e6, "write": 34.60e6},
+    "fwd": {"src": "59cf1e42472eff90", "read": 55.59e6, "write": 20.45e6},
 }
 
 

@@ -42,13 +42,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Position of workgroup `bid` in a heaviest-first list of tiles, rearranged so
 // that the workgroups one CU holds at the same time carry about equal work.  A
 // fresh grid is dealt breadth-first: CU c receives workgroups c, c + ncu,
-// c + 2 ncu, ... (measured on MI355X).  While the first `resident` rounds of ncu
-// workgroups are all in flight together, odd rounds take the list backwards, so
-// a CU that got one of the heaviest tiles in round 0 gets one of the lightest of
-// round 1.  The reversal moves whole blocks of 8, which keeps bid mod 8 (the
-// XCD a workgroup lands on, and with it the head's shared L2).  Later rounds,
-// dispatched as CUs free up, and grids whose CU count is not a multiple of 8,
-// keep the plain order (as does an unknown CU count, ncu <= 0).
+// c + 2 ncu, ... (measured on MI355X).  While the first `resident` passes of ncu
+// workgroups are all in flight together, odd passes take the list backwards, so
+// a CU that got one of the heaviest tiles of the first pass gets one of the
+// lightest of the second.  The reversal moves whole blocks of 8, which keeps
+// bid mod 8 (the XCD a workgroup lands on, and with it the head's shared L2).
+// Later passes, dispatched as CUs free up, and grids whose CU count is not a
+// multiple of 8 keep the plain order (as does an unknown CU count, ncu <= 0).
 __device__ __forceinline__ int balanced_rank(int bid, int nwg, int ncu, int resident) {
   if (ncu <= 0 || (ncu & 7) != 0) return bid;
   const int j = bid / ncu, c = bid % ncu;
