@@ -504,6 +504,8 @@ def main():
                     help="only time decode attention (for profiling its kernels)")
     ap.add_argument("--composed-only", action="store_true",
                     help="only time the composed path (for profiling its kernels)")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="only time the ragged batch and the same batch padded (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (for counter calibration)")
     args = ap.parse_args()
@@ -528,6 +530,10 @@ def main():
     if args.decode_only:
         wd = inputs.DECODE_WORKLOADS[inputs.DECODE_BENCH]
         print(json.dumps({"decode": run_decode(wd, args.steps, args.warmup)}), flush=True)
+        return
+    if args.ragged_only:
+        print(json.dumps({"ragged": run_ragged(inputs.RAGGED_BENCH, args.steps, args.warmup)}),
+              flush=True)
         return
     fl = counted_flops(w)
     r = run_gpu(w, args.steps, args.warmup)
