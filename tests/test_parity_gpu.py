@@ -170,3 +170,27 @@ def test_long_sequence_prefix_and_identities(dtype, ref):
     kd = float(np.sum(k[0, 0] * gpu["dk"][0, 0]))
     mag = float(np.sum(np.abs(q[0] * gpu["dq"][0])))
     assert abs(qd - kd) <= tau * mag, f"q.dq {qd} != k.dk {kd} (magnitude {mag})"
+
+
+@pytest.mark.parametrize("dtype,slices", [("bf16", 2), ("f32", 6)])
+def test_gqa_group_split_in_slices(dtype, slices, ref):
+    """A group of 6 query heads over 16 * 2 * 8 = 256 key tiles: the dk/dv kernel
+    splits each group into `slices` workgroups (bf16: 2 slices of 3 heads, fp32:
+    6 of 1), whose partial sums a second kernel adds in a fixed order.  Checked
+    on sampled (batch, kv head) units."""
+    from bwd_head_rms_amd import _lib
+    B, S, Hq, Hkv, hd = 16, 1024, 12, 2, 64
+    code = _lib.BF16 if dtype == "bf16" else _lib.F32
+    base = 8 * B * Hq * S
+    assert _lib.lib().xattn_bwd_workspace_bytes(B, S, Hq, Hkv, hd, code) == \
+        base + 2 * 4 * slices * B * Hkv * S * hd, "unexpected split"
+    arrs = inputs.generate(B, S, Hq, Hkv, hd, seed=66, shaped=True, dtype=dtype)
+    gpu = H.gpu_run(arrs, dtype, None)
+    units = [0, 17, 31]
+    outs = [ref.run(arrs["q"], arrs["k"], arrs["v"], arrs["dO"], units=(u, u + 1)) for u in units]
+    merged = {n: np.where(np.isnan(outs[0][n]), 0.0, outs[0][n]) for n in H.NAMES}
+    for o in outs[1:]:
+        for n in H.NAMES:
+            merged[n] = np.where(np.isnan(o[n]), merged[n], o[n])
+    H.compare(gpu, merged, dtype, f"GQA group 6 in {slices} slices", units=units, Hkv=Hkv,
+              group=Hq // Hkv)
