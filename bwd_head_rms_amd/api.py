@@ -114,24 +114,27 @@ def bwd(q, k, v, o, lse, dO, scale=None, dq=None, dk=None, dv=None, workspace=No
 
 
 class CausalAttention(torch.autograd.Function):
-    """autograd wrapper: o = causal_attention(q, k, v); grads are fp32 cast to the input dtype."""
+    """autograd wrapper: o = causal_attention(q, k, v); grads are fp32 cast to the input dtype.
+    With `lens` (int32 device tensor [B]) the batch is right-padded: padding rows of o are zero
+    and padding inputs get zero gradients."""
 
     @staticmethod
-    def forward(ctx, q, k, v, scale=None):
-        o, lse = fwd(q, k, v, scale)
+    def forward(ctx, q, k, v, scale=None, lens=None):
+        o, lse = fwd(q, k, v, scale, lens=lens)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.scale = scale
+        ctx.lens = lens
         return o
 
     @staticmethod
     def backward(ctx, dO):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, o, lse, dO.contiguous().to(q.dtype), ctx.scale)
-        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None
+        dq, dk, dv = bwd(q, k, v, o, lse, dO.contiguous().to(q.dtype), ctx.scale, lens=ctx.lens)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
 
 
-def causal_attention(q, k, v, scale=None):
-    return CausalAttention.apply(q, k, v, scale)
+def causal_attention(q, k, v, scale=None, lens=None):
+    return CausalAttention.apply(q, k, v, scale, lens)
 
 
 def qknorm_rope_fwd(x, w, eps=1e-6, rope_base=10000.0, out=None):
@@ -174,6 +177,28 @@ def qknorm_rope_bwd(x, w, dout, eps=1e-6, rope_base=10000.0, dx=None, dw=None, w
                                       _code(x), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), _stream(x)))
     return dx, dw
+
+
+class QKNormRope(torch.autograd.Function):
+    """autograd wrapper of the per-head RMS QK-norm + RoPE step:
+    y [B,H,S,hd] = qknorm_rope(x [B,S,H,hd], w [hd]); dx is cast to x's dtype, dw stays fp32."""
+
+    @staticmethod
+    def forward(ctx, x, w, eps=1e-6, rope_base=10000.0):
+        ctx.save_for_backward(x, w)
+        ctx.eps, ctx.rope_base = eps, rope_base
+        return qknorm_rope_fwd(x, w, eps=eps, rope_base=rope_base)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w = ctx.saved_tensors
+        dx, dw = qknorm_rope_bwd(x, w, dy.contiguous().float(), eps=ctx.eps,
+                                 rope_base=ctx.rope_base)
+        return dx.to(x.dtype), dw, None, None
+
+
+def qknorm_rope(x, w, eps=1e-6, rope_base=10000.0):
+    return QKNormRope.apply(x, w, eps, rope_base)
 
 
 def decode_workspace_bytes(B, T, H, Hkv, hd):
