@@ -17,7 +17,8 @@
 // result is bitwise reproducible (the deterministic group sum of the
 // "xtrain evolution overview", infra table row T15).  D comes from the dq
 // kernel, which runs first on the same stream.  Work order: heaviest key tiles
-// (those near the start of the sequence) first.
+// (those near the start of the sequence) first, dealt so that the two
+// workgroups a CU holds at once carry about equal work.
 #include <type_traits>
 
 #include "attn_device.hpp"
@@ -47,8 +48,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ lse, const T* __restrict__ dO, const float* __restrict__ dws,
     float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ part,
-    const int* __restrict__ lens, int B, int S, int H, int Hkv, int nkt, int BG, int R, float c,
-    float scale) {
+    const int* __restrict__ lens, int B, int S, int H, int Hkv, int nkt, int BG, int R, int ncu,
+    float c, float scale) {
   using C = DkvCfg<T, HD>;
   using M = Mma<T>;
   __shared__ __align__(16) T sQ[2][C::TILE];
@@ -58,8 +59,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 31, g = lane >> 5;
-  const int bid = blockIdx.x;
-  const int kt = bid / (BG * R);  // key tile 0 (the heaviest) first
+  // key tile 0 (the heaviest) first, balanced over the two workgroups a CU
+  // holds at once (two waves per SIMD)
+  const int bid = balanced_rank(blockIdx.x, gridDim.x, ncu, 2);
+  const int kt = bid / (BG * R);
   const int bg = bid % BG;
   const int rs = (bid / BG) % R;  // which of the R slices of the group's query heads
   const int b = bg / Hkv, kvh = bg % Hkv;
@@ -390,7 +393,7 @@ static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* 
   dim3 grid((unsigned)(nkt * BG * R)), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, part, lens, d.B,
-                     d.S, d.H, d.Hkv, nkt, BG, R, scale * kLog2e, scale);
+                     d.S, d.H, d.Hkv, nkt, BG, R, device_cu_count(), scale * kLog2e, scale);
   if (R > 1) {
     const long n4 = (long)d.B * d.Hkv * d.S * HD / 4;
     hipLaunchKernelGGL(dkdv_group_sum_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256),

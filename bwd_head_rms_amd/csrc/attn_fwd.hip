@@ -544,7 +544,7 @@ static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v
 }
 
 // Compute units of the current device, read once per device.
-static int device_cu_count() {
+int device_cu_count() {
   constexpr int kMaxDevices = 64;
   static std::atomic<int> cached[kMaxDevices] = {};
   int dev = 0;

@@ -31,6 +31,9 @@ void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, con
                      const float* lse, const void* dO, float* dws, float* dk, float* dv,
                      const int* lens, float scale, hipStream_t stream);
 int dkdv_split(const Dims& d, int dtype);
+
+// Compute units of the current device (0 if it cannot be read), cached per device.
+int device_cu_count();
 size_t dkdv_part_offset(const Dims& d);
 
 // Per-head RMS QK-norm + rotary embedding.  x [B][S][H][hd] (token-major),
