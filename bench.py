@@ -56,9 +56,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "1b81d2450cbf39a1", "read": 84.86e6, "write": 67.14e6},
-    "dq": {"src": "2b3aca3ca37b7832", "read": 109.27e6, "write": 34.60e6},
-    "fwd": {"src": "59cf1e42472eff90", "read": 55.59e6, "write": 20.45e6},
+    "dkdv": {"src": "4d006ba2db979998", "read": 85.99e6, "write": 67.52e6},
+    "dq": {"src": "a9b3721bf0a51d15", "read": 123.29e6, "write": 34.61e6},
+    "fwd": {"src": "ab90e5e878c83c1e", "read": 55.90e6, "write": 20.45e6},
 }
 
 
