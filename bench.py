@@ -56,9 +56,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "4d006ba2db979998", "read": 85.99e6, "write": 67.52e6},
-    "dq": {"src": "a9b3721bf0a51d15", "read": 123.29e6, "write": 34.61e6},
-    "fwd": {"src": "ab90e5e878c83c1e", "read": 55.90e6, "write": 20.45e6},
+    "dkdv": {"src": "a86760d1d316f635", "read": 85.79e6, "write": 67.32e6},
+    "dq": {"src": "a9b3721bf0a51d15", "read": 114.27e6, "write": 34.60e6},
+    "fwd": {"src": "ab90e5e878c83c1e", "read": 55.58e6, "write": 20.45e6},
 }
 
 
@@ -75,6 +75,9 @@ def kernel_source_hash(kernel):
     # compile flags without the include paths, which differ between checkouts
     flags = [f for f in build.COMMON + build.DEVICE_FLAGS if not os.path.isabs(f)]
     h.update(" ".join(flags).encode())
+    extra = build.SOURCE_FLAGS.get(KERNEL_FILES[kernel], [])
+    if extra:
+        h.update((" " + " ".join(extra)).encode())
     return h.hexdigest()[:16]
 
 
