@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libxattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["attn_fwd.hip", "attn_bwd_dq.hip", "attn_bwd_dkdv.hip", "qknorm_rope.hip",
-           "decode_attn.hip", "composed.hip", "api.cpp"]
+           "decode_attn.hip", "composed.hip", "plan.cpp", "api.cpp"]
 
 # Packed-fp32 VALU instructions are switched off for all device code.  MFMA
 # accumulators are kept in ordinary VGPRs: the kernels post-process every score
@@ -25,8 +25,10 @@ SOURCES = ["attn_fwd.hip", "attn_bwd_dq.hip", "attn_bwd_dkdv.hip", "qknorm_rope.
 # between the two register files.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+# Any inline-assembly warning (e.g. a statement that clobbers a register the
+# compiler reserves) fails the build.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
-          "-Wall", "-Wno-unused-function"]
+          "-Wall", "-Wno-unused-function", "-Werror=inline-asm"]
 # Per-source additions.  The dK/dV kernel is scheduled for instruction-level
 # parallelism rather than occupancy (it runs two waves per SIMD either way, at
 # 180 + 64 registers instead of 170 + 64): measured 1-3% faster on the

@@ -1,9 +1,10 @@
 // api.cpp -- the C ABI of libxattn.so (declared in include/xattn.h).
 //
-// Every argument is checked here, on the host, before any HIP call; only a
-// fully valid call enqueues kernels.  The library holds no state: no handles,
-// no allocations, no synchronisation.
-#include <hip/hip_runtime.h>
+// Every argument is checked here, on the host, before any HIP call, including
+// the grid of every launch the call would make (sized by plan.cpp, as the
+// launchers size them); only a fully valid call enqueues kernels.  The library
+// holds no state: no handles, no allocations, no synchronisation.
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstdint>
@@ -14,25 +15,26 @@
 
 namespace {
 
-constexpr int kTileRows = 128;  // rows per workgroup in every kernel (4 waves x 32)
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_shape(int B, int S, int H, int Hkv, int hd) {
+// dtype must already be valid.
+int check_shape(int B, int S, int H, int Hkv, int hd, int dtype) {
   if (B <= 0 || S <= 0 || H <= 0 || Hkv <= 0 || hd <= 0) return XATTN_ERR_SHAPE;
   if (H % Hkv != 0) return XATTN_ERR_GQA;
   if (hd != 16 && hd != 32 && hd != 64) return XATTN_ERR_HEAD_DIM;
   const int64_t plane = (int64_t)S * hd;  // elements of one (batch, head) plane
   if (plane > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
-  const int64_t tiles = ((int64_t)S + kTileRows - 1) / kTileRows;
-  if (tiles * B * H > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
   if ((int64_t)B * H * S > std::numeric_limits<int64_t>::max() / 8) return XATTN_ERR_SHAPE;
+  // every launch of the forward and backward fits one HIP grid
+  const xattn::AttnPlan p = xattn::attn_plan(xattn::Dims{B, S, H, Hkv, hd}, dtype);
+  for (const long long n : {p.fwd_blocks, p.dq_blocks, p.dkdv_blocks, p.dkdv_sum_blocks})
+    if (n > xattn::kMaxBlocks) return XATTN_ERR_SHAPE;
   return XATTN_OK;
 }
 
 int check_common(int B, int S, int H, int Hkv, int hd, float scale, int dtype) {
   if (dtype != XATTN_F32 && dtype != XATTN_BF16) return XATTN_ERR_DTYPE;
-  const int rc = check_shape(B, S, H, Hkv, hd);
+  const int rc = check_shape(B, S, H, Hkv, hd, dtype);
   if (rc != XATTN_OK) return rc;
   if (!std::isfinite(scale) || !(scale > 0.f)) return XATTN_ERR_SCALE;
   return XATTN_OK;
@@ -123,13 +125,10 @@ int xattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, 
 
 size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype) {
   if (dtype != XATTN_F32 && dtype != XATTN_BF16) return 0;
-  if (check_shape(B, S, H, Hkv, hd) != XATTN_OK) return 0;
-  const xattn::Dims d{B, S, H, Hkv, hd};
-  const int R = xattn::dkdv_split(d, dtype);
-  if (R == 1) return 2 * sizeof(float) * (size_t)B * (size_t)H * (size_t)S;  // D and LSE*log2e
-  // plus the partial dk, dv of a group split over workgroups
-  return sizeof(float) * (xattn::dkdv_part_offset(d) +
-                          2 * (size_t)R * (size_t)B * (size_t)Hkv * (size_t)S * (size_t)hd);
+  if (check_shape(B, S, H, Hkv, hd, dtype) != XATTN_OK) return 0;
+  // D and LSE*log2e per query row, plus the partial dk, dv of a group split
+  // over workgroups
+  return xattn::attn_plan(xattn::Dims{B, S, H, Hkv, hd}, dtype).workspace_bytes;
 }
 
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -241,8 +240,8 @@ int check_decode(int B, int T, int H, int Hkv, int hd, float scale, int dtype) {
   if ((int64_t)T * hd > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
   if (T > xattn::kDecodeMaxT) return XATTN_ERR_SHAPE;
   if ((int64_t)B * H * hd > std::numeric_limits<int32_t>::max()) return XATTN_ERR_SHAPE;
-  if (xattn::decode_plan(B, T, H, Hkv, hd).blocks > std::numeric_limits<int32_t>::max())
-    return XATTN_ERR_SHAPE;
+  const xattn::DecodePlan p = xattn::decode_plan(B, T, H, Hkv, hd);
+  if (p.blocks > xattn::kMaxBlocks || p.combine_blocks > xattn::kMaxBlocks) return XATTN_ERR_SHAPE;
   if (!std::isfinite(scale) || !(scale > 0.f)) return XATTN_ERR_SCALE;
   return XATTN_OK;
 }
@@ -280,6 +279,8 @@ int xattn_composed_fwd(const void* q, const void* k, const void* v, void* o, flo
   if (!q || !k || !v || !o || !lse || !p) return XATTN_ERR_NULL;
   const int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
   if (rc != XATTN_OK) return rc;
+  if (xattn::composed_max_blocks(xattn::Dims{B, S, H, Hkv, hd}) > xattn::kMaxBlocks)
+    return XATTN_ERR_SHAPE;
   if (p_bytes < xattn_composed_buffer_bytes(B, S, H)) return XATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
       !aligned16(p))
@@ -296,6 +297,8 @@ int xattn_composed_bwd(const void* q, const void* k, const void* v, const float*
   if (!q || !k || !v || !p || !dO || !dq || !dk || !dv || !ds) return XATTN_ERR_NULL;
   const int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
   if (rc != XATTN_OK) return rc;
+  if (xattn::composed_max_blocks(xattn::Dims{B, S, H, Hkv, hd}) > xattn::kMaxBlocks)
+    return XATTN_ERR_SHAPE;
   const size_t need = xattn_composed_buffer_bytes(B, S, H);
   if (p_bytes < need || ds_bytes < need) return XATTN_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(p) || !aligned16(dO) ||

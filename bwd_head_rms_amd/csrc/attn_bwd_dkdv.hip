@@ -336,19 +336,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
     }
 }
 
-constexpr long kDkvSplitBelow = 512;  // kv tiles under which a group is split
-// Workgroups a split aims for.  Each slice adds a partial dK, dV plane to
-// write and re-read; the fp32 kernel spends longer per tile, so it gains from
-// more slices than bf16 loses to the extra traffic.
-constexpr long kDkvSplitTargetF32 = 1024, kDkvSplitTargetBf16 = 512;
-
 // dk = sum over r of part_k[r], dv = sum over r of part_v[r], r ascending
 // (the group sum of a split group), four floats per thread.
-__global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(kThreads) void dkdv_group_sum_kernel(const float* __restrict__ part,
                                                              float* __restrict__ dk,
                                                              float* __restrict__ dv, long n4,
                                                              int R) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long i = (long)blockIdx.x * kThreads + threadIdx.x;
   if (i >= 2 * n4) return;
   const bool is_v = i >= n4;
   const long e = is_v ? i - n4 : i;
@@ -361,42 +355,25 @@ __global__ __launch_bounds__(256) void dkdv_group_sum_kernel(const float* __rest
   reinterpret_cast<float4*>(is_v ? dv : dk)[e] = a;
 }
 
-int dkdv_split(const Dims& d, int dtype) {
-  const int group = d.H / d.Hkv;
-  const long tiles = (long)d.B * d.Hkv * ((d.S + 127) / 128);
-  if (group == 1 || tiles >= kDkvSplitBelow) return 1;
-  // fewer workgroups than two per CU: split each group into the fewest slices
-  // (a divisor of the group) that reach the target
-  const long target = dtype == 0 ? kDkvSplitTargetF32 : kDkvSplitTargetBf16;
-  int R = 1;
-  while (R < group && tiles * R < target) {
-    do { ++R; } while (group % R != 0);
-  }
-  return R;
-}
-
-size_t dkdv_part_offset(const Dims& d) {
-  return (2 * (size_t)d.B * d.H * d.S + 3) / 4 * 4;  // floats, keeps 16-byte alignment
-}
-
 template <typename T, int HD>
 static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* v,
                        const float* lse, const void* dO, float* dws, float* dk, float* dv,
                        const int* lens, float scale, hipStream_t stream) {
   using C = DkvCfg<T, HD>;
-  static_assert(C::BN == 128, "dkdv_split assumes 128-key tiles");
+  static_assert(C::BN == kDkvTileKeys && C::NT == kThreads, "tiling differs from the plan");
+  const AttnPlan p = attn_plan(d, sizeof(T) == 4 ? 0 : 1);
   const int nkt = (d.S + C::BN - 1) / C::BN;
   const int BG = d.B * d.Hkv;
-  const int R = dkdv_split(d, sizeof(T) == 4 ? 0 : 1);
+  const int R = p.split;
   // the partials follow the per-row statistics in the workspace
   float* part = R > 1 ? dws + dkdv_part_offset(d) : nullptr;
-  dim3 grid((unsigned)(nkt * BG * R)), block(C::NT);
+  dim3 grid((unsigned)p.dkdv_blocks), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, lse, (const T*)dO, dws, dk, dv, part, lens, d.B,
                      d.S, d.H, d.Hkv, nkt, BG, R, device_cu_count(), scale * kLog2e, scale);
   if (R > 1) {
     const long n4 = (long)d.B * d.Hkv * d.S * HD / 4;
-    hipLaunchKernelGGL(dkdv_group_sum_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256),
+    hipLaunchKernelGGL(dkdv_group_sum_kernel, dim3((unsigned)p.dkdv_sum_blocks), dim3(kThreads),
                        0, stream, (const float*)part, dk, dv, n4, R);
   }
 }

@@ -215,9 +215,11 @@ static void dq_typed(const Dims& d, const void* q, const void* k, const void* v,
                      const float* lse, const void* dO, float* dq, float* dws, const int* lens,
                      float scale, hipStream_t stream) {
   using C = DqCfg<T, HD>;
+  static_assert(C::BM == dq_tile_rows(sizeof(T) == 4 ? 0 : 1) && C::NT <= kThreads,
+                "tiling differs from the plan");
   const int nqt = (d.S + C::BM - 1) / C::BM;
   const int BH = d.B * d.H;
-  dim3 grid((unsigned)(nqt * BH)), block(C::NT);
+  dim3 grid((unsigned)attn_plan(d, sizeof(T) == 4 ? 0 : 1).dq_blocks), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, (const T*)o, lse, (const T*)dO, dq, dws, lens, d.S,
                      d.H, d.Hkv, nqt, BH, scale * kLog2e, scale);

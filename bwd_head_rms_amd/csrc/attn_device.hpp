@@ -173,24 +173,32 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
 // (buffer_load_dwordx4 / _dword with lds, LDS base in M0).  The whole offset
 // is passed in the VGPR operand, the part of the address that the buffer range
 // check covers (the SGPR offset is added after the check), so every byte at or
-// past the end of the resource reads as zero.  Written as inline
-// assembly so that the compiler does not treat a copy in flight into one buffer
-// as a hazard for reads of the other buffer (it would otherwise wait for the
-// copy before every LDS read); completion is awaited explicitly
-// (wait_global_loads) before the barrier that publishes the tile.
+// past the end of the resource reads as zero.
+//
+// The LDS base is an input operand bound to M0 ("{m0}"): the compiler itself
+// writes M0 before the statement and knows it is read there, so M0 is never
+// changed behind its back.  The leading s_nop is the one wait state an M0
+// write needs before an LDS DMA reads it (the compiler's hazard check does not
+// look inside assembly).  The copy is assembly rather than the compiler's
+// buffer-load-to-LDS builtin because with the builtin the compiler cannot tell
+// a copy into one ring slot from reads of another and waits for every copy in
+// flight before the first LDS read that follows it, which serialises the
+// next tile's copy with the arithmetic on the current one.  Completion is
+// awaited explicitly (wait_global_loads) before the barrier that publishes a
+// tile.
 __device__ __forceinline__ void lds_copy16(v4i rsrc, uint32_t voff, const void* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(base)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "{m0}"(base)
+               : "memory");
 }
 __device__ __forceinline__ void lds_copy4(v4i rsrc, uint32_t voff, const void* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(base)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "{m0}"(base)
+               : "memory");
 }
 
 template <typename T, int HD, int ROWS>

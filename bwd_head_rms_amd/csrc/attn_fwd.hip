@@ -535,9 +535,10 @@ template <typename T, int HD>
 static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v, void* o,
                       float* lse, const int* lens, float scale, hipStream_t stream) {
   using C = FwdCfg<T, HD>;
+  static_assert(C::BM == kFwdTileRows && C::NT == kThreads, "tiling differs from the plan");
   const int nqt = (d.S + C::BM - 1) / C::BM;
   const int BH = d.B * d.H;
-  dim3 grid((unsigned)(nqt * BH)), block(C::NT);
+  dim3 grid((unsigned)attn_plan(d, 0).fwd_blocks), block(C::NT);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, block, 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, (T*)o, lse, lens, d.S, d.H, d.Hkv,
                      nqt, BH, scale * kLog2e);
@@ -562,9 +563,10 @@ template <int HD>
 static void fwd_pipe(const Dims& d, const void* q, const void* k, const void* v, void* o,
                      float* lse, const int* lens, float scale, hipStream_t stream) {
   using P = FwdPipe<HD>;
+  static_assert(P::BM == kFwdTileRows && P::NT == kThreads, "tiling differs from the plan");
   const int nqt = (d.S + P::BM - 1) / P::BM;
   const int BH = d.B * d.H;
-  dim3 grid((unsigned)(nqt * BH)), block(P::NT);
+  dim3 grid((unsigned)attn_plan(d, 1).fwd_blocks), block(P::NT);
   hipLaunchKernelGGL((attn_fwd_pipe_kernel<HD>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, lens, d.S,
                      d.H, d.Hkv, nqt, BH, device_cu_count(), scale * kLog2e);

@@ -33,7 +33,6 @@
 
 namespace xattn {
 
-constexpr int kCmpTile = 128;  // rows and keys per workgroup tile (4 waves x 32)
 
 // --------------------------------------------------------------------------
 // out[bh][i][j] = c * a[bh][i] . bm[kv][j] on the lower-triangle tiles

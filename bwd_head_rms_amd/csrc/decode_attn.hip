@@ -34,8 +34,6 @@ namespace xattn {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kDecMaxChunk = 1024;
-constexpr int kDecMinChunk = 256;
 // Most chunks per sequence the merge kernel takes (its LDS holds one weight per
 // chunk); longer caches use longer chunks.
 constexpr int kDecMaxChunkRecords = 4096;
@@ -417,37 +415,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_combine_kernel(
   }
 }
 
-static int heads_per_wg(int group) {
-  for (int gc = 8; gc > 1; gc /= 2)
-    if (group % gc == 0) return gc;
-  return 1;
-}
-
-DecodePlan decode_plan(int B, int T, int H, int Hkv, int hd) {
-  const int group = H / Hkv;
-  const long units = (long)B * Hkv * (group / heads_per_wg(group));
-  int chunk = kDecMinChunk;
-  // about four workgroups per CU (one resident wave of them), chunks as short as that allows
-  while (chunk < kDecMaxChunk && units * ((T + chunk - 1) / chunk) > 1024) chunk *= 2;
-  DecodePlan p;
-  p.chunk = chunk;
-  p.nsplit = (T + chunk - 1) / chunk;
-  p.blocks = p.nsplit * units;
-  p.part_bytes = p.nsplit > 1 ? sizeof(float) * (size_t)B * H * p.nsplit * (hd + 2) : 0;
-  return p;
-}
-
 template <typename T, int HD, int GC>
 static void decode_launch(const Dims& d, const DecodePlan& p, const void* q, const void* k,
                           const void* v, const int* lens, void* o, float* lse, float* part,
                           float scale, hipStream_t stream) {
   const int group = d.H / d.Hkv;
-  const dim3 grid((unsigned)((long)p.nsplit * d.B * d.Hkv * (group / GC)));
+  const dim3 grid((unsigned)p.blocks);
   hipLaunchKernelGGL((decode_attn_kernel<T, HD, GC>), grid, dim3(kDecThreads), 0, stream,
                      (const T*)q, (const T*)k, (const T*)v, lens, (T*)o, lse, part, d.S, d.H,
                      d.Hkv, group, p.nsplit, p.chunk, scale * kLog2e);
   if (p.nsplit > 1) {
-    hipLaunchKernelGGL((decode_combine_kernel<T, HD>), dim3((unsigned)(d.B * d.H)),
+    hipLaunchKernelGGL((decode_combine_kernel<T, HD>), dim3((unsigned)p.combine_blocks),
                        dim3(kDecThreads), 0, stream, part, (T*)o, lse, p.nsplit);
   }
 }
@@ -456,7 +434,7 @@ template <typename T, int HD>
 static void decode_hd(const Dims& d, const DecodePlan& p, const void* q, const void* k,
                       const void* v, const int* lens, void* o, float* lse, float* part,
                       float scale, hipStream_t stream) {
-  switch (heads_per_wg(d.H / d.Hkv)) {
+  switch (p.heads_per_wg) {
     case 8: decode_launch<T, HD, 8>(d, p, q, k, v, lens, o, lse, part, scale, stream); break;
     case 4: decode_launch<T, HD, 4>(d, p, q, k, v, lens, o, lse, part, scale, stream); break;
     case 2: decode_launch<T, HD, 2>(d, p, q, k, v, lens, o, lse, part, scale, stream); break;

@@ -1,13 +1,40 @@
 // launch.hpp -- host-side launchers of the attention kernels (one per kernel
-// family), called by the C ABI after it has validated every argument.
+// family), called by the C ABI after it has validated every argument, and the
+// launch sizing they share with that validation (plan.cpp).
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+
+#include <stddef.h>
 
 namespace xattn {
 
 struct Dims {
   int B, S, H, Hkv, hd;
 };
+
+// Threads per workgroup of every kernel in the library.
+constexpr int kThreads = 256;
+// HIP takes at most 2^32 - 1 work-items in one launch: with kThreads per
+// workgroup, at most this many workgroups.
+constexpr long long kMaxBlocks = 0xFFFFFFFFLL / kThreads;
+
+// Tiling of the attention kernels (each kernel static_asserts its own).
+constexpr int kFwdTileRows = 128;  // query rows per forward workgroup
+// query rows per dq workgroup: fp32 runs two waves, bf16 four
+constexpr int dq_tile_rows(int dtype) { return dtype == 0 ? 64 : 128; }
+constexpr int kDkvTileKeys = 128;  // keys per dk/dv workgroup
+constexpr int kCmpTile = 128;      // rows and keys per composed-path tile
+
+// Workgroups of each launch one attention call makes, and its workspace.
+struct AttnPlan {
+  long long fwd_blocks, dq_blocks, dkdv_blocks, dkdv_sum_blocks;
+  int split;               // slices a GQA group is split into by the dk/dv kernel
+  size_t workspace_bytes;  // backward workspace
+};
+AttnPlan attn_plan(const Dims& d, int dtype);
+
+// Largest grid of the composed path's launches.
+long long composed_max_blocks(const Dims& d);
 
 // `lens` ([B] int32 on the device, or NULL): sequence b holds lens[b] rows
 // (clamped to [0, S]) of its right-padded S-row planes; rows and keys past it
@@ -66,11 +93,14 @@ void launch_composed_bwd(int dtype, const Dims& d, const void* q, const void* k,
 
 // Decode attention: q, o [B][H][hd]; k, v [B][Hkv][T][hd] with T in Dims::S;
 // lens [B] (nullable); part is the workspace (nullable when part_bytes == 0).
+constexpr int kDecMinChunk = 256, kDecMaxChunk = 1024;  // cache positions per workgroup
 struct DecodePlan {
-  int chunk;          // cache positions per workgroup
-  int nsplit;         // chunks per sequence
-  long blocks;        // workgroups of the main kernel
-  size_t part_bytes;  // workspace: partial records when nsplit > 1
+  int chunk;            // cache positions per workgroup
+  int nsplit;           // chunks per sequence
+  int heads_per_wg;     // query heads of a GQA group one workgroup serves
+  long blocks;          // workgroups of the main kernel
+  long combine_blocks;  // workgroups of the merge kernel (0: no merge)
+  size_t part_bytes;    // workspace: partial records when nsplit > 1
 };
 DecodePlan decode_plan(int B, int T, int H, int Hkv, int hd);
 

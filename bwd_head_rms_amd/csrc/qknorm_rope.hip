@@ -222,12 +222,6 @@ __global__ __launch_bounds__(kReduceThreads) void qknorm_dw_reduce_kernel(
   if (t == 0) dw[d] = t_sum[0];
 }
 
-int qknorm_bwd_blocks(long nvec, int hd) {
-  const long threads = nvec * (hd / 8);
-  const long blocks = (threads + 255) / 256;
-  return (int)(blocks < kNormMaxBlocks ? blocks : kNormMaxBlocks);
-}
-
 template <typename T, int HD>
 static void norm_fwd_typed(const NormDims& d, const void* x, const float* w, void* out,
                            float eps, float base, hipStream_t stream) {

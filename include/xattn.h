@@ -49,8 +49,11 @@
  *
  * Supported: hd in {16, 32, 64}; any S >= 1; H a multiple of Hkv; scale a
  *   positive finite number; every data pointer 16-byte aligned; every tensor
- *   below 2^31 elements per (batch, head) plane and B*H*ceil(S/128) below
- *   2^31 workgroups.
+ *   below 2^31 elements per (batch, head) plane; and every kernel launch a
+ *   call makes within HIP's limit of 2^32 - 1 work-items, i.e. at most
+ *   16777215 workgroups of 256 threads (the forward launches B*H*ceil(S/128)
+ *   of them, the fp32 dq kernel B*H*ceil(S/64); larger shapes return
+ *   XATTN_ERR_SHAPE before anything is enqueued).
  */
 #ifndef XATTN_H
 #define XATTN_H
@@ -146,7 +149,6 @@ int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse
                    float scale, int dtype, void* workspace, size_t workspace_bytes,
                    void* stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
 /*
  * Per-head RMS QK-norm + rotary position embedding: the step that turns a q (or
  * k) projection output into the attention input (the per-head QK-norm of the
@@ -281,6 +283,7 @@ int xattn_decode(const void* q, const void* k, const void* v, const int* lens, v
                  float* lse, int B, int T, int H, int Hkv, int hd, float scale, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Static, NUL-terminated description of a status code (never NULL). */
 const char* xattn_strerror(int status);
 
 #ifdef __cplusplus
