@@ -12,7 +12,7 @@ SYMBOLS = ("xattn_fwd", "xattn_bwd", "xattn_bwd_workspace_bytes", "xattn_bwd_dq"
            "xattn_bwd_dkdv", "xattn_qknorm_rope_fwd", "xattn_qknorm_rope_bwd_workspace_bytes",
            "xattn_qknorm_rope_bwd", "xattn_decode_workspace_bytes", "xattn_decode",
            "xattn_fwd_ragged", "xattn_bwd_ragged", "xattn_composed_buffer_bytes",
-           "xattn_composed_fwd", "xattn_composed_bwd",
+           "xattn_composed_fwd", "xattn_composed_bwd", "xattn_bwd_noalloc",
            "xattn_strerror")
 
 F32, BF16 = 0, 1
@@ -20,6 +20,7 @@ STATUS = {
     0: "XATTN_OK", 1: "XATTN_ERR_NULL", 2: "XATTN_ERR_SHAPE", 3: "XATTN_ERR_GQA",
     4: "XATTN_ERR_HEAD_DIM", 5: "XATTN_ERR_DTYPE", 6: "XATTN_ERR_WORKSPACE",
     7: "XATTN_ERR_SCALE", 8: "XATTN_ERR_HIP", 9: "XATTN_ERR_ALIGN", 10: "XATTN_ERR_PARAM",
+    11: "XATTN_ERR_SCRATCH",
 }
 
 
@@ -71,6 +72,8 @@ def lib():
     L.xattn_decode_workspace_bytes.restype = sz
     L.xattn_decode.argtypes = [vp] * 6 + [i, i, i, i, i, f, i, vp, sz, vp]
     L.xattn_decode.restype = i
+    L.xattn_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, vp]
+    L.xattn_bwd_noalloc.restype = i
     L.xattn_strerror.argtypes = [i]
     L.xattn_strerror.restype = ctypes.c_char_p
     _lib = L

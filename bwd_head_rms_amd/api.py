@@ -113,6 +113,28 @@ def bwd(q, k, v, o, lse, dO, scale=None, dq=None, dk=None, dv=None, workspace=No
     return dq, dk, dv
 
 
+def bwd_noalloc(q, k, v, o, lse, dO, scale, dq, dk, dv):
+    """Causal attention backward through ``xattn_bwd_noalloc``: the caller
+    passes every output (fp32 dq [B,H,S,hd], dk, dv [B,Hkv,S,hd]) and nothing
+    is allocated, by this wrapper or the library (its scratch is a fixed device
+    array: B*H*S at most 2097152 query rows; calls that overlap on one GPU
+    race on it).  Arguments as in ``bwd``."""
+    B, S, H, Hkv, hd = _dims(q, k)
+    dt = q.dtype
+    for t, n, shp in ((q, "q", (B, H, S, hd)), (k, "k", (B, Hkv, S, hd)), (v, "v", (B, Hkv, S, hd)),
+                      (o, "o", (B, H, S, hd)), (dO, "dO", (B, H, S, hd))):
+        _check_tensor(t, n, shp, dt)
+    _check_tensor(lse, "lse", (B, H, S), torch.float32)
+    _check_tensor(dq, "dq", (B, H, S, hd), torch.float32)
+    _check_tensor(dk, "dk", (B, Hkv, S, hd), torch.float32)
+    _check_tensor(dv, "dv", (B, Hkv, S, hd), torch.float32)
+    check(lib().xattn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), dO.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), B, S, H, Hkv, hd, float(scale), _code(q),
+                                  _stream(q)))
+    return dq, dk, dv
+
+
 class CausalAttention(torch.autograd.Function):
     """autograd wrapper: o = causal_attention(q, k, v); grads are fp32 cast to the input dtype.
     With `lens` (int32 device tensor [B]) the batch is right-padded: padding rows of o are zero

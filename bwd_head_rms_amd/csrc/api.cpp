@@ -94,7 +94,7 @@ int bwd_dkdv_impl(const void* q, const void* k, const void* v, const float* lse,
     return XATTN_ERR_ALIGN;
   xattn::launch_bwd_dkdv(dtype, xattn::Dims{B, S, H, Hkv, hd}, q, k, v, lse, dO,
                          static_cast<float*>(workspace), dk, dv, lens, scale,
-                         static_cast<hipStream_t>(stream));
+                         /*split_groups=*/true, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -152,6 +152,32 @@ int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               void* stream) {
   return bwd_impl(q, k, v, o, lse, dO, nullptr, dq, dk, dv, B, S, H, Hkv, hd, scale, dtype,
                   workspace, workspace_bytes, stream);
+}
+
+int xattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dO, float* dq, float* dk, float* dv, int B, int S, int H,
+                      int Hkv, int hd, float scale, int dtype, void* stream) {
+  // the checks of xattn_bwd, all before anything is enqueued
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return XATTN_ERR_NULL;
+  const int rc = check_common(B, S, H, Hkv, hd, scale, dtype);
+  if (rc != XATTN_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dO) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return XATTN_ERR_ALIGN;
+  // GQA groups stay whole (no partial dk, dv planes): the per-row part only
+  const xattn::Dims d{B, S, H, Hkv, hd};
+  if (xattn::attn_plan(d, dtype, /*split_groups=*/false).workspace_bytes >
+      xattn::kNoAllocScratchBytes)
+    return XATTN_ERR_SCRATCH;
+  float* ws = xattn::noalloc_scratch();
+  if (!ws) return XATTN_ERR_HIP;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  xattn::launch_bwd_dq(dtype, d, q, k, v, o, lse, dO, dq, ws, nullptr, scale, st);
+  int s2 = launch_status();
+  if (s2 != XATTN_OK) return s2;
+  xattn::launch_bwd_dkdv(dtype, d, q, k, v, lse, dO, ws, dk, dv, nullptr, scale,
+                         /*split_groups=*/false, st);
+  return launch_status();
 }
 
 int xattn_fwd_ragged(const void* q, const void* k, const void* v, const int* lens, void* o,
@@ -322,6 +348,8 @@ const char* xattn_strerror(int status) {
     case XATTN_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case XATTN_ERR_ALIGN: return "a data pointer is not 16-byte aligned";
     case XATTN_ERR_PARAM: return "eps must be finite and >= 0, and the rope base finite and > 1";
+    case XATTN_ERR_SCRATCH:
+      return "shape too large for the fixed scratch of xattn_bwd_noalloc (8*B*H*S bytes above 16 MiB)";
     default: return "unknown xattn status";
   }
 }

@@ -358,10 +358,10 @@ __global__ __launch_bounds__(kThreads) void dkdv_group_sum_kernel(const float* _
 template <typename T, int HD>
 static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* v,
                        const float* lse, const void* dO, float* dws, float* dk, float* dv,
-                       const int* lens, float scale, hipStream_t stream) {
+                       const int* lens, float scale, bool split_groups, hipStream_t stream) {
   using C = DkvCfg<T, HD>;
   static_assert(C::BN == kDkvTileKeys && C::NT == kThreads, "tiling differs from the plan");
-  const AttnPlan p = attn_plan(d, sizeof(T) == 4 ? 0 : 1);
+  const AttnPlan p = attn_plan(d, sizeof(T) == 4 ? 0 : 1, split_groups);
   const int nkt = (d.S + C::BN - 1) / C::BN;
   const int BG = d.B * d.Hkv;
   const int R = p.split;
@@ -380,15 +380,15 @@ static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* 
 
 void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,
                      const float* lse, const void* dO, float* dws, float* dk, float* dv,
-                     const int* lens, float scale, hipStream_t stream) {
+                     const int* lens, float scale, bool split_groups, hipStream_t stream) {
   if (dtype == 0) {
-    if (d.hd == 16) dkdv_typed<float, 16>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
-    else if (d.hd == 32) dkdv_typed<float, 32>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
-    else dkdv_typed<float, 64>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
+    if (d.hd == 16) dkdv_typed<float, 16>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, split_groups, stream);
+    else if (d.hd == 32) dkdv_typed<float, 32>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, split_groups, stream);
+    else dkdv_typed<float, 64>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, split_groups, stream);
   } else {
-    if (d.hd == 16) dkdv_typed<bf16, 16>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
-    else if (d.hd == 32) dkdv_typed<bf16, 32>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
-    else dkdv_typed<bf16, 64>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, stream);
+    if (d.hd == 16) dkdv_typed<bf16, 16>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, split_groups, stream);
+    else if (d.hd == 32) dkdv_typed<bf16, 32>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, split_groups, stream);
+    else dkdv_typed<bf16, 64>(d, q, k, v, lse, dO, dws, dk, dv, lens, scale, split_groups, stream);
   }
 }
 

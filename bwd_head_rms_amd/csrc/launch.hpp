@@ -31,7 +31,9 @@ struct AttnPlan {
   int split;               // slices a GQA group is split into by the dk/dv kernel
   size_t workspace_bytes;  // backward workspace
 };
-AttnPlan attn_plan(const Dims& d, int dtype);
+// split_groups = false keeps each GQA group in one dk/dv workgroup (split = 1),
+// so the workspace is the per-row part only.
+AttnPlan attn_plan(const Dims& d, int dtype, bool split_groups = true);
 
 // Largest grid of the composed path's launches.
 long long composed_max_blocks(const Dims& d);
@@ -50,13 +52,19 @@ void launch_bwd_dq(int dtype, const Dims& d, const void* q, const void* k, const
                    const int* lens, float scale, hipStream_t stream);
 
 // Backward, second kernel: dk, dv (group-summed), reading D from `dws`.  When
-// dkdv_split(d, dtype) > 1 the query heads of a group are spread over workgroups that
-// write partial dk, dv into `dws` at dkdv_part_offset(d) floats
-// ([2][group][B][Hkv][S][hd]), summed in ascending head order by a second
-// kernel.
+// split_groups and dkdv_split(d, dtype) > 1 the query heads of a group are
+// spread over workgroups that write partial dk, dv into `dws` at
+// dkdv_part_offset(d) floats ([2][group][B][Hkv][S][hd]), summed in ascending
+// head order by a second kernel.
 void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, const void* v,
                      const float* lse, const void* dO, float* dws, float* dk, float* dv,
-                     const int* lens, float scale, hipStream_t stream);
+                     const int* lens, float scale, bool split_groups, hipStream_t stream);
+
+// Device address of the fixed scratch array of the allocation-free backward on
+// the current device (looked up once per device), or NULL if it cannot be
+// read.  Holds kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+float* noalloc_scratch();
 int dkdv_split(const Dims& d, int dtype);
 
 // Compute units of the current device (0 if it cannot be read), cached per device.

@@ -46,12 +46,12 @@ size_t dkdv_part_offset(const Dims& d) {
   return (2 * (size_t)d.B * d.H * d.S + 3) / 4 * 4;  // floats, keeps 16-byte alignment
 }
 
-AttnPlan attn_plan(const Dims& d, int dtype) {
+AttnPlan attn_plan(const Dims& d, int dtype, bool split_groups) {
   AttnPlan p;
   const long long BH = (long long)d.B * d.H, BG = (long long)d.B * d.Hkv;
   p.fwd_blocks = cdiv(d.S, kFwdTileRows) * BH;
   p.dq_blocks = cdiv(d.S, dq_tile_rows(dtype)) * BH;
-  p.split = dkdv_split(d, dtype);
+  p.split = split_groups ? dkdv_split(d, dtype) : 1;
   p.dkdv_blocks = cdiv(d.S, kDkvTileKeys) * BG * p.split;
   // the partial-sum kernel: 4 floats per thread over dk and dv
   p.dkdv_sum_blocks = p.split > 1 ? cdiv(2 * (BG * d.S * d.hd / 4), kThreads) : 0;

@@ -80,7 +80,8 @@ typedef enum {
   XATTN_ERR_SCALE = 7,      /* scale not positive and finite */
   XATTN_ERR_HIP = 8,        /* the HIP runtime rejected a kernel launch */
   XATTN_ERR_ALIGN = 9,      /* a data pointer is not 16-byte aligned */
-  XATTN_ERR_PARAM = 10      /* eps or rope base out of range (QK-norm + RoPE) */
+  XATTN_ERR_PARAM = 10,     /* eps or rope base out of range (QK-norm + RoPE) */
+  XATTN_ERR_SCRATCH = 11    /* too large for xattn_bwd_noalloc's fixed scratch */
 } xattn_status;
 
 /*
@@ -148,6 +149,32 @@ int xattn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse
                    const void* dO, float* dk, float* dv, int B, int S, int H, int Hkv, int hd,
                    float scale, int dtype, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * xattn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It allocates nothing (no hipMalloc, no allocating
+ * library call): the per-row scratch (-D and LSE * log2(e), 8*B*H*S bytes)
+ * lives in a fixed 16 MiB device array inside the library, one per GPU,
+ * held from the first call on that GPU until the process ends.
+ *   Arguments, layout, dtypes and the result are those of xattn_bwd, except
+ *   that the query heads of a GQA group are never split over workgroups (the
+ *   dk, dv group sum runs in one workgroup per key tile, in the same fixed
+ *   order), so it needs no room for partial sums.
+ *   Limit: 8*B*H*S <= 16777216 (B*H*S <= 2097152 query rows); larger shapes
+ *   return XATTN_ERR_SCRATCH before anything is enqueued.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (e.g. on two streams without ordering between them) race and give
+ *   wrong results.  Nothing in the array needs to start at zero (the first
+ *   kernel writes every value the second reads).
+ *   The first call on each GPU looks up the array's device address (no
+ *   allocation, no synchronisation); make it outside a graph capture.
+ * Returns an xattn_status.
+ */
+int xattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, float* dq, float* dk, float* dv,
+                      int B, int S, int H, int Hkv, int hd, float scale, int dtype,
+                      void* stream);
 
 /*
  * Per-head RMS QK-norm + rotary position embedding: the step that turns a q (or

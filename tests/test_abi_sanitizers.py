@@ -28,6 +28,7 @@ DRIVER = r"""
 
 static int g_launches = 0;
 static bool g_fail = false;  // the next hipGetLastError reports a failure
+static bool g_no_scratch = false;  // the scratch address lookup fails
 
 hipError_t hipGetLastError() {
   const bool f = g_fail;
@@ -43,9 +44,11 @@ void launch_bwd_dq(int, const Dims&, const void*, const void*, const void*, cons
   ++g_launches;
 }
 void launch_bwd_dkdv(int, const Dims&, const void*, const void*, const void*, const float*,
-                     const void*, float*, float*, float*, const int*, float, hipStream_t) {
+                     const void*, float*, float*, float*, const int*, float, bool, hipStream_t) {
   ++g_launches;
 }
+alignas(256) static float g_scratch_stub[64];
+float* noalloc_scratch() { return g_no_scratch ? nullptr : g_scratch_stub; }
 int device_cu_count() { return 256; }
 void launch_qknorm_rope_fwd(int, const NormDims&, const void*, const float*, void*, float, float,
                             hipStream_t) { ++g_launches; }
@@ -192,6 +195,32 @@ int main() {
   EXPECT(xattn_bwd_dq(q, k, v, o, lse, nullptr, dq, 2, 100, 4, 2, 64, 0.125f, 1, ws, need, nullptr),
          XATTN_ERR_NULL, 0);
 
+  // --- allocation-free backward: same checks, plus the fixed scratch's limit
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 2, 64, 0.125f, 1, nullptr),
+         XATTN_OK, 2);
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 16, 1024, 8, 2, 64, 0.125f, 0, nullptr),
+         XATTN_OK, 2);
+  // 8 * B * H * S = 16 MiB exactly, then one query row more per head
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 1, 131072, 16, 16, 64, 0.125f, 1,
+                           nullptr), XATTN_OK, 2);
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 1, 131073, 16, 16, 64, 0.125f, 1,
+                           nullptr), XATTN_ERR_SCRATCH, 0);
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, nullptr, 2, 100, 4, 2, 64, 0.125f, 1,
+                           nullptr), XATTN_ERR_NULL, 0);
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, (float*)mis, dv, 2, 100, 4, 2, 64, 0.125f, 1,
+                           nullptr), XATTN_ERR_ALIGN, 0);
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 2, 64, 0.125f, 5, nullptr),
+         XATTN_ERR_DTYPE, 0);
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 2, 64, nan, 1, nullptr),
+         XATTN_ERR_SCALE, 0);
+  g_no_scratch = true;
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 2, 64, 0.125f, 1, nullptr),
+         XATTN_ERR_HIP, 0);
+  g_no_scratch = false;
+  g_fail = true;
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 2, 64, 0.125f, 1, nullptr),
+         XATTN_ERR_HIP, 1);
+
   // --- QK-norm + RoPE
   const float* w = f[12];
   const size_t nws = xattn_qknorm_rope_bwd_workspace_bytes(2, 64, 4, 64);
@@ -263,11 +292,11 @@ int main() {
                             0.125f, 1, nullptr), XATTN_ERR_NULL, 0);
 
   // --- status text: never NULL, distinct for the defined codes
-  const char* seen[11] = {};
+  const char* seen[12] = {};
   for (int s = -2; s <= 12; ++s) {
     const char* t = xattn_strerror(s);
     if (!t || !*t) { std::printf("FAIL strerror(%d)\n", s); ++g_failures; }
-    if (s >= 0 && s <= 10) {
+    if (s >= 0 && s <= 11) {
       for (int u = 0; u < s; ++u)
         if (std::strcmp(seen[u], t) == 0) { std::printf("FAIL strerror dup %d\n", s); ++g_failures; }
       seen[s] = t;
