@@ -160,6 +160,38 @@ def time_loop(fn, steps):
     return ms
 
 
+def alg_bytes(w):
+    """Algorithmic HBM bytes of one fwd+bwd step: every input read once and
+    every output written once by each pass (fwd: q, k, v in, o and lse out;
+    bwd: q, k, v, o, dO, lse in, fp32 dq, dk, dv out).  The per-row workspace
+    is implementation overhead and not counted."""
+    e = 2 if w.dtype == "bf16" else 4
+    nq = w.B * w.H * w.S * w.hd
+    nk = w.B * w.Hkv * w.S * w.hd
+    rows = w.B * w.H * w.S
+    fwd = e * (nq + 2 * nk) + e * nq + 4 * rows
+    bwd = e * (3 * nq + 2 * nk) + 4 * rows + 4 * (nq + 2 * nk)
+    return fwd + bwd
+
+
+def step_roofline(w, ms_per_step):
+    """The step against its own roofline: the time bound is the larger of the
+    counted FLOPs at the dtype's dense MFMA peak and the algorithmic bytes at
+    the HBM peak; frac = bound / measured time."""
+    fl = counted_flops(w)["total"]
+    by = alg_bytes(w)
+    t_mfma = fl / (PEAK_TFLOPS[w.dtype] * 1e12)
+    t_hbm = by / (PEAK_HBM_GBPS * 1e9)
+    sec = ms_per_step / 1e3
+    if t_mfma >= t_hbm:
+        return {"bound": "mfma", "achieved": round(fl / sec / 1e12, 3), "peak": PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": round(t_mfma / sec, 5), "t_bound_us": round(t_mfma * 1e6, 2),
+                "alg_bytes": by}
+    return {"bound": "hbm", "achieved": round(by / sec / 1e9, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(t_hbm / sec, 5), "t_bound_us": round(t_hbm * 1e6, 2),
+            "alg_bytes": by}
+
+
 def counted_flops(w):
     nnz = w.S * (w.S + 1) / 2
     per = w.B * w.H * nnz * w.hd
@@ -233,6 +265,19 @@ def run_gpu(w, steps, warmup):
             "device": torch.cuda.get_device_name(dev)}
 
 
+def run_secondary(w, steps, warmup):
+    """One workload's fwd+bwd step, as the headline one is measured."""
+    r = run_gpu(w, steps, warmup)
+    sec = r["ms_per_step"] / 1e3
+    tf = counted_flops(w)["total"] / sec / 1e12
+    return {"workload": w.name, "dtype": w.dtype, "B": w.B, "S": w.S, "H": w.H, "Hkv": w.Hkv,
+            "hd": w.hd, "ms_per_step": round(r["ms_per_step"], 5),
+            "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in r["kernel_ms"].items()},
+            "tflops": round(tf, 3), "pct_of_mfma_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 3),
+            "tokens_per_s": round(w.B * w.S / sec, 1),
+            "roofline": step_roofline(w, r["ms_per_step"])}
+
+
 def norm_bytes(w):
     """Algorithmic HBM bytes of the QK-norm + RoPE step on the q input of `w`:
     fwd reads x and writes out (input dtype); bwd reads x (input dtype) and
@@ -288,6 +333,33 @@ def run_norm(w, steps, warmup):
             "roofline": {"bound": "hbm", **roof}}
 
 
+def host_cpu():
+    """The host CPU: model name, physical cores and logical CPUs (from
+    /proc/cpuinfo) and the CPUs this process may run on."""
+    model, cores = None, set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model is None:
+                    model = v
+                elif k == "physical id":
+                    phys = v
+                elif k == "core id":
+                    core = v
+                elif not k and phys is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    return {"cpu_model": model, "physical_cores": len(cores) or None,
+            "logical_cpus": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, budget_units=None):
     """Time the fp64 oracle on whole (batch, kv head) units of the workload."""
     import numpy as np
@@ -316,7 +388,7 @@ def cpu_baseline(w, budget_units=None):
         ref.set_threads(0)
     flops1 = 14 * nnz * w.hd * (w.H // w.Hkv)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
+            "seconds": dt, "threads_used": threads, **host_cpu(),
             "sample": f"{n_units} of {w.B * w.Hkv} (batch, kv head) units of {w.name} "
                       f"({n_units * (w.H // w.Hkv)} heads x S={w.S}, fwd+bwd, fp64)",
             "single_thread": {"value": flops1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
@@ -567,6 +639,7 @@ def main():
         "fwd_tflops": round(fl["fwd"] / (km["fwd"] / 1e3) / 1e12, 3),
         "bwd_tflops": round(fl["bwd"] / ((km["dq"] + km["dkdv"]) / 1e3) / 1e12, 3),
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in km.items()},
+        "step_roofline": step_roofline(w, r["ms_per_step"]),
         "roofline": {"bound": "mfma", "kernel": KERNEL_NAMES[dom],
                      "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(ach / peak, 5), "traffic": measured_traffic(dom, w.name),
@@ -574,15 +647,9 @@ def main():
         "device": r["device"],
     }
     if not args.no_secondary and args.workload is None:
-        w2 = inputs.WORKLOADS["dim384_b16_s256_h12_hd32_f32"]
-        r2 = run_gpu(w2, args.steps, args.warmup)
-        s2 = r2["ms_per_step"] / 1e3
-        t2 = counted_flops(w2)["total"] / s2 / 1e12
-        out["secondary"] = {"workload": w2.name, "dtype": w2.dtype, "tflops": round(t2, 3),
-                            "pct_of_mfma_peak": round(100 * t2 / PEAK_TFLOPS[w2.dtype], 3),
-                            "ms_per_step": round(r2["ms_per_step"], 5),
-                            "tokens_per_s": round(w2.B * w2.S / s2, 1),
-                            "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in r2["kernel_ms"].items()}}
+        # every other workload of the metric, each a full fwd+bwd step of its own
+        out["secondary"] = [run_secondary(inputs.WORKLOADS[n], args.steps, args.warmup)
+                            for n in inputs.WORKLOADS if n != w.name]
     if not args.no_next:
         out["next_rows"] = {
             "qknorm_rope": run_norm(w, args.steps, args.warmup),

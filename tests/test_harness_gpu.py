@@ -82,5 +82,12 @@ def test_bench_cli_emits_contract_json():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0
+    assert cb["threads_used"] >= 1 and cb["logical_cpus"] >= 1 and "cpu_model" in cb
+    # every other workload of the metric, each with its own roofline
+    sec = {e["workload"]: e for e in d["secondary"]}
+    assert set(sec) == set(inputs.WORKLOADS) - {inputs.LONG_CONTEXT}
+    for e in sec.values():
+        assert e["ms_per_step"] > 0 and set(e["kernel_avg_us"]) == {"fwd", "dq", "dkdv"}
+        assert e["roofline"]["bound"] in ("mfma", "hbm") and 0 < e["roofline"]["frac"] <= 1
     assert np.isfinite(d["value"]) and d["value"] > 0
     Hh.log(f"  bench JSON ok: value {d['value']} {d['unit']}")
