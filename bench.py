@@ -4,11 +4,13 @@ One step = one pass of the whole path over one batch of the synthetic
 long-context workload (B4, S2048, 16 heads of 64, bf16 in / fp32 accumulate):
 xattn_fwd, then the backward as its two kernels (xattn_bwd_dq, xattn_bwd_dkdv,
 which together are exactly xattn_bwd), all through the C ABI on torch's current
-stream with inputs resident in HBM.  W untimed warmup steps, then K timed steps
-between synchronisations.  HIP events between the kernels (timing-only events
-without a system-scope fence, so no cache flush separates the kernels) give
-each kernel's average duration inside the timed region; the dominant kernel's
-roofline is reported against MI355X's dense bf16 MFMA peak.
+stream with inputs resident in HBM.  At least W untimed warmup steps (and at
+least WARMUP_MIN_S seconds of them), then K timed steps between
+synchronisations.  HIP events around the dk/dv kernel, the longest one
+(timing-only events without a system-scope fence, so no cache flush separates
+the kernels), give its average duration inside the timed region, and its
+roofline is reported against MI355X's dense bf16 MFMA peak; the forward and dq
+kernels are timed in loops of their own after the timed region.
 
 Counted FLOPs (the FlashAttention-2 convention, causal half only):
     fwd 4*hd*nnz, bwd 10*hd*nnz per (batch, head), nnz = S(S+1)/2
@@ -56,9 +58,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "a86760d1d316f635", "read": 85.79e6, "write": 67.32e6},
-    "dq": {"src": "a9b3721bf0a51d15", "read": 114.27e6, "write": 34.60e6},
-    "fwd": {"src": "ab90e5e878c83c1e", "read": 55.58e6, "write": 20.45e6},
+    "dkdv": {"src": "35443810aeeec5d1", "read": 85.88e6, "write": 67.37e6},
+    "dq": {"src": "3115b7c76d6a21bc", "read": 114.88e6, "write": 34.61e6},
+    "fwd": {"src": "2885462a638d5b9b", "read": 55.49e6, "write": 20.45e6},
 }
 
 
@@ -140,6 +142,28 @@ class TimingEvents:
         for e in self._made:
             self._hip.hipEventDestroy(e)
         self._made = []
+
+
+# Warm-up lasts at least this long whatever W is: the first milliseconds of
+# work after idle run slower (measured on MI355X: the long-context step at
+# 222-224 us after 5 warm-up steps, 202 us after 50).
+WARMUP_MIN_S = 0.3
+
+
+def warm_up(step, warmup):
+    """Run `step` at least `warmup` times and for at least WARMUP_MIN_S seconds
+    of GPU time; returns (steps run, seconds)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < WARMUP_MIN_S:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()  # keeps the host from running far ahead of the GPU
+    torch.cuda.synchronize()
+    return n, time.perf_counter() - t0
 
 
 def time_loop(fn, steps):
@@ -235,33 +259,34 @@ def run_gpu(w, steps, warmup):
         _lib.check(L.xattn_bwd_dkdv(p["q"], p["k"], p["v"], p["lse"], p["dO"], p["dk"], p["dv"],
                                     *dims, p["ws"], ws_bytes, sh))
 
-    for _ in range(warmup):
-        fwd(); bwd_dq(); bwd_dkdv()
-    torch.cuda.synchronize()
+    warm_steps, warm_s = warm_up(lambda: (fwd(), bwd_dq(), bwd_dkdv()), warmup)
 
+    # Timed region: exactly `steps` steps.  Timing events sit only around the
+    # dk/dv kernel (the roofline's kernel): every event recorded between two
+    # kernels lengthens the step by about a microsecond, which on the short
+    # workloads is several percent of it.
     T = TimingEvents()
-    ev = [[T.new() for _ in range(4)] for _ in range(steps)]
+    e_start = T.new()
+    ev = [[T.new() for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    T.record(e_start, sh)
     for i in range(steps):
-        T.record(ev[i][0], sh)
         fwd()
-        T.record(ev[i][1], sh)
         bwd_dq()
-        T.record(ev[i][2], sh)
+        T.record(ev[i][0], sh)
         bwd_dkdv()
-        T.record(ev[i][3], sh)
+        T.record(ev[i][1], sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = T.ms(ev[0][0], ev[-1][3])
-    per = {"fwd": [], "dq": [], "dkdv": []}
-    for e in ev:
-        per["fwd"].append(T.ms(e[0], e[1]))
-        per["dq"].append(T.ms(e[1], e[2]))
-        per["dkdv"].append(T.ms(e[2], e[3]))
+    total_ms = T.ms(e_start, ev[-1][1])
+    dkdv_ms = float(np.mean([T.ms(e[0], e[1]) for e in ev]))
     T.close()
-    avg = {k: float(np.mean(v)) for k, v in per.items()}
+    # the other two kernels' durations, each timed over `steps` back-to-back
+    # launches after the timed region (context, not part of the step's time)
+    avg = {"fwd": time_loop(fwd, steps), "dq": time_loop(bwd_dq, steps), "dkdv": dkdv_ms}
     return {"ms_per_step": total_ms / steps, "wall_s": wall, "kernel_ms": avg,
+            "warmup_steps": warm_steps, "warmup_s": round(warm_s, 3),
             "device": torch.cuda.get_device_name(dev)}
 
 
@@ -617,7 +642,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     km = r["kernel_ms"]
     kflops = {"fwd": fl["k_fwd"], "dq": fl["k_dq"], "dkdv": fl["k_dkdv"]}
-    dom = max(km, key=km.get)
+    dom = "dkdv"  # the longest kernel, timed by events inside the timed region
     ach = kflops[dom] / (km[dom] / 1e3) / 1e12
     out = {
         "metric": METRIC,
@@ -639,6 +664,10 @@ def main():
         "fwd_tflops": round(fl["fwd"] / (km["fwd"] / 1e3) / 1e12, 3),
         "bwd_tflops": round(fl["bwd"] / ((km["dq"] + km["dkdv"]) / 1e3) / 1e12, 3),
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in km.items()},
+        "kernel_timing": "dkdv: events around it in every timed step; fwd, dq: loops of K "
+                         "launches each, after the timed region",
+        "warmup_run": {"steps": r["warmup_steps"], "seconds": r["warmup_s"],
+                       "min_seconds": WARMUP_MIN_S},
         "step_roofline": step_roofline(w, r["ms_per_step"]),
         "roofline": {"bound": "mfma", "kernel": KERNEL_NAMES[dom],
                      "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",

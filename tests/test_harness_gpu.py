@@ -75,6 +75,9 @@ def test_bench_cli_emits_contract_json():
               "cpu_baseline"):
         assert k in d, f"missing {k}"
     assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
+    # warm-up: at least the W steps asked for, and at least its minimum duration
+    wr = d["warmup_run"]
+    assert wr["steps"] >= 1 and wr["seconds"] >= wr["min_seconds"] > 0
     assert d["config"]["workload"] == inputs.LONG_CONTEXT and d["dtype"] == "bf16"
     rf = d["roofline"]
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
