@@ -60,7 +60,7 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 MEASURED_TRAFFIC = {
     "dkdv": {"src": "35443810aeeec5d1", "read": 85.88e6, "write": 67.37e6},
     "dq": {"src": "3115b7c76d6a21bc", "read": 114.88e6, "write": 34.61e6},
-    "fwd": {"src": "2885462a638d5b9b", "read": 55.49e6, "write": 20.45e6},
+    "fwd": {"src": "62e8ad5813f9995e", "read": 51.17e6, "write": 20.45e6},
 }
 
 
