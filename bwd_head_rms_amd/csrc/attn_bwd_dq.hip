@@ -80,27 +80,34 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     stV.issue(vp, 0, n, sV[0], wave, lane, tid);
   }
 
-  typename M::frag qf[C::NKS], df[C::NKS];
+  // Every per-row load goes out before any use, so they share one round trip:
+  // a row past the sequence end reads row n-1 and its operands are zeroed.
+  const int lrow = q_ok ? my_q : n - 1;
+  typename M::frag qf[C::NKS], df[C::NKS], of[C::NKS];
+  row_frags_global<T, HD>(q + qplane + (size_t)lrow * HD, g, qf);
+  row_frags_global<T, HD>(dO + qplane + (size_t)lrow * HD, g, df);
+  row_frags_global<T, HD>(o + qplane + (size_t)lrow * HD, g, of);
+  const float lse_row = lse[(size_t)bh * S + lrow];
   float Dp = 0.f;
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) {
-    if (q_ok) {
-      qf[ks] = row_frag_global<T, HD>(q + qplane + (size_t)my_q * HD, g, ks);
-      df[ks] = row_frag_global<T, HD>(dO + qplane + (size_t)my_q * HD, g, ks);
-      const typename M::frag of = row_frag_global<T, HD>(o + qplane + (size_t)my_q * HD, g, ks);
-      if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) Dp += (float)of[t] * (float)df[ks][t];
-      } else {
-        Dp += of * df[ks];
-      }
+      for (int t = 0; t < 8; ++t) Dp += (float)of[ks][t] * (float)df[ks][t];
     } else {
+      Dp += of[ks] * df[ks];
+    }
+  }
+  if (!q_ok) {
+    Dp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
       qf[ks] = zero_frag<T>();
       df[ks] = zero_frag<T>();
     }
   }
   const float Drow = halves_sum(Dp);
-  const float lse2 = q_ok ? lse[(size_t)bh * S + my_q] * kLog2e : 0.f;
+  const float lse2 = q_ok ? lse_row * kLog2e : 0.f;
   if (q_ok && g == 0) {
     dws[(size_t)bh * S + my_q] = -Drow;  // negated: the dk/dv kernel starts dP from it
     dws[(size_t)BH * S + (size_t)bh * S + my_q] = lse2;  // for the dk/dv kernel

@@ -145,6 +145,31 @@ __device__ __forceinline__ typename Mma<T>::frag row_frag_global(const T* row, i
   }
 }
 
+// All head-dimension operands of one row, f[ks] = row_frag_global(row, g, ks),
+// with 16-byte loads: bf16 one per operand, fp32 one per four operands (a
+// lane's elements g*HD/2 .. g*HD/2 + HD/2 - 1 are contiguous).  Every row of a
+// 16-byte aligned plane is 16-byte aligned.
+template <typename T, int HD>
+__device__ __forceinline__ void row_frags_global(const T* row, int g,
+                                                 typename Mma<T>::frag (&f)[HD / Mma<T>::KSTEP]) {
+  constexpr int NKS = HD / Mma<T>::KSTEP;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) f[ks] = row_frag_global<T, HD>(row, g, ks);
+  } else {
+    static_assert(NKS % 4 == 0, "fp32 operands come in fours");
+    const float4* p = reinterpret_cast<const float4*>(row + g * (HD / 2));
+#pragma unroll
+    for (int i = 0; i < NKS / 4; ++i) {
+      const float4 u = p[i];
+      f[4 * i] = u.x;
+      f[4 * i + 1] = u.y;
+      f[4 * i + 2] = u.z;
+      f[4 * i + 3] = u.w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LDS tiles of ROWS x HD elements.
 //

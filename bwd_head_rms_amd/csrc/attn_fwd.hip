@@ -94,10 +94,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
   // padding rows of this tile are written first, while nothing is live
   if (!q_ok && g == 0 && my_q < S) store_padding_row<T, HD>(o, lse, bh, S, my_q);
 
+  // the query operands by wide loads; a row past the sequence end reads row
+  // n-1 and its operands are zeroed
   typename M::frag qf[C::NKS];
+  row_frags_global<T, HD>(qp + (size_t)(q_ok ? my_q : n - 1) * HD, g, qf);
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks)
-    qf[ks] = q_ok ? row_frag_global<T, HD>(qp + (size_t)my_q * HD, g, ks) : zero_frag<T>();
+  for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = q_ok ? qf[ks] : zero_frag<T>();
 
   f32x16 oacc[C::ND];
 #pragma unroll
@@ -173,17 +175,16 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
         }
       };
       scores();
-      probs();
       // Each row keeps a reference max m and uses it as long as its weights
       // stay below 2^kRescaleSlack (their sum bounds every weight).  Only when
       // that fails -- the row's first tile (m = -inf), or scores that really
       // outgrew m -- are the scores recomputed, the row max taken and the
       // accumulator rescaled.  The decision is per row (rows that pass keep m
       // and recompute the same weights), so every row's result depends only
-      // on that row's scores.
-      const bool fail = halves_max(tsum <= kRescaleBound ? 0.f : 1.f) != 0.f;
-      if (__ballot(fail)) {
-        scores();
+      // on that row's scores.  Every row fails on the first tile (key 0 is
+      // visible to all rows), so there m is the tile's row max directly, with
+      // nothing to rescale.
+      if (j == 0) {
         float mx = -INFINITY;
 #pragma unroll
         for (int cb = 0; cb < C::NB; ++cb)
@@ -191,14 +192,29 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
           }
-        mx = halves_max(mx) * c;
-        const float m_new = fail ? fmaxf(m, mx) : m;
-        const float alpha = fail ? fast_exp2(m - m_new) : 1.f;
-        m = m_new;
-        l *= alpha;
-#pragma unroll
-        for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
+        m = halves_max(mx) * c;
         probs();
+      } else {
+        probs();
+        const bool fail = halves_max(tsum <= kRescaleBound ? 0.f : 1.f) != 0.f;
+        if (__ballot(fail)) {
+          scores();
+          float mx = -INFINITY;
+#pragma unroll
+          for (int cb = 0; cb < C::NB; ++cb)
+            if (act[cb]) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[cb][r]);
+            }
+          mx = halves_max(mx) * c;
+          const float m_new = fail ? fmaxf(m, mx) : m;
+          const float alpha = fail ? fast_exp2(m - m_new) : 1.f;
+          m = m_new;
+          l *= alpha;
+#pragma unroll
+          for (int d = 0; d < C::ND; ++d) oacc[d] *= alpha;
+          probs();
+        }
       }
       l += tsum;
 #pragma unroll
