@@ -85,7 +85,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
     return;
   }
 
-  const int kv0 = kt * C::BN + wave * 32;
+  // The key block a wave owns follows its SIMD: block s for SIMD s in the first
+  // workgroup a CU holds (blockIdx below the CU count), block 3 - s in the
+  // second.  Causal key blocks near the start of a tile carry the most query
+  // blocks, so each SIMD pairs a heavy block of one workgroup with a light
+  // block of the other (at S = 256: 8 + 1, 7 + 2, 6 + 3, 5 + 4 query blocks,
+  // where wave-index order put 8 + 3 on one SIMD).  Any placement gives a
+  // permutation of the blocks, so the results do not depend on it.
+  __shared__ int simd_of[C::NW];
+  const int rank = simd_rank<C::NW>(wave, lane, simd_of);
+  const int kb_w = ncu > 0 && (blockIdx.x / ncu) % 2 == 1 ? C::NW - 1 - rank : rank;
+  const int kv0 = kt * C::BN + kb_w * 32;
   const int my_kv = kv0 + li;
   const bool kv_ok = my_kv < n;
   const bool wave_live = kv0 < n;
@@ -131,10 +141,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
   // copies after them)
   if constexpr (sizeof(T) == 2) issue(0, 0);
   typename M::frag kf[C::NKS], vf[C::NKS];
+  if constexpr (sizeof(T) == 4 && HD <= 32) {
+    // fp32: four operands per 16-byte load (a key past the sequence end reads
+    // key n-1 and its operands are zeroed); at hd 64 the wide loads' registers
+    // would cost a wave per SIMD
+    const size_t krow = (size_t)(kv_ok ? my_kv : n - 1) * HD;
+    row_frags_global<T, HD>(k + kvplane + krow, g, kf);
+    row_frags_global<T, HD>(v + kvplane + krow, g, vf);
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-    kf[ks] = kv_ok ? row_frag_global<T, HD>(k + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
-    vf[ks] = kv_ok ? row_frag_global<T, HD>(v + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      kf[ks] = kv_ok ? kf[ks] : zero_frag<T>();
+      vf[ks] = kv_ok ? vf[ks] : zero_frag<T>();
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      kf[ks] = kv_ok ? row_frag_global<T, HD>(k + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
+      vf[ks] = kv_ok ? row_frag_global<T, HD>(v + kvplane + (size_t)my_kv * HD, g, ks) : zero_frag<T>();
+    }
   }
 
   // dK^T / dV^T accumulators live for the whole kernel: bf16 keeps them in AGPRs

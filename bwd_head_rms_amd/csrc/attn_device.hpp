@@ -56,6 +56,29 @@ __device__ __forceinline__ int balanced_rank(int bid, int nwg, int ncu, int resi
   return j * ncu + (ncu - 8 - (c & ~7)) + (c & 7);
 }
 
+// SIMD (0-3) of the compute unit that runs this wave: bits 5:4 of HW_ID.
+__device__ __forceinline__ int wave_simd() {
+  return (__builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11)) >> 4) & 3;
+}
+
+// Rank of this wave among the workgroup's NW waves ordered by (SIMD, wave
+// index): a permutation of 0 .. NW-1 whatever the placement.  With NW = 4 and
+// one wave on each SIMD of the CU it is the SIMD itself.  `scratch` holds NW
+// ints of LDS; the call contains a workgroup barrier.
+template <int NW>
+__device__ __forceinline__ int simd_rank(int wave, int lane, int* scratch) {
+  const int s = wave_simd();
+  if (lane == 0) scratch[wave] = s;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int s2 = scratch[w];
+    r += (s2 < s || (s2 == s && w < wave)) ? 1 : 0;
+  }
+  return r;
+}
+
 // Combine lanes l and l^32 (v_permlane32_swap exchanges the two half-waves: the
 // two results hold x of lanes 0..31 and 32..63 in every lane's position).
 __device__ __forceinline__ float halves_max(float x) {
