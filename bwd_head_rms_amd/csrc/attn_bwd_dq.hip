@@ -1,7 +1,7 @@
 // attn_bwd_dq.hip -- causal attention backward, query side, for gfx950.
 //
-// One workgroup (4 waves) per (batch, head, 128-row query tile); each wave owns
-// 32 query rows, as in the forward.  The prologue computes
+// One workgroup (4 waves; fp32 at hd 64: 2) per (batch, head, query tile of 32
+// rows per wave); each wave owns 32 query rows, as in the forward.  The prologue computes
 //   D_i = sum_d dO_id * o_id
 // (the simplification of the softmax Jacobian in the fused kernel of the
 // "xtrain evolution overview", infra table row T14) and stores it for the
@@ -25,12 +25,13 @@ namespace xattn {
 
 template <typename T, int HD>
 struct DqCfg {
-  // fp32 runs two waves (64 query rows) per workgroup: its kernel then has a
-  // register budget of its own (277 + 21 at hd 64, one wave per SIMD) instead
-  // of fitting four waves into 256, and at hd 64 runs a third faster
-  // (measured: GQA fp32 workload 481 -> 314 us; no change at hd 32); bf16
-  // keeps four waves
-  static constexpr int NW = sizeof(T) == 4 ? 2 : 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
+  // fp32 at hd 64 runs two waves (64 query rows) per workgroup: its kernel
+  // then has a register budget of its own (277 + 21, one wave per SIMD)
+  // instead of fitting four waves into 256, and runs a third faster
+  // (measured: GQA fp32 workload 481 -> 314 us).  Everything else runs four,
+  // one on each SIMD of the CU.
+  static constexpr int NW = sizeof(T) == 4 && HD == 64 ? 2 : 4, NT = NW * kWave, BM = 32 * NW,
+                       BN = 64, NB = BN / 32;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;
   static constexpr int NAS = 32 / Mma<T>::KSTEP;
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ o, const float* __restrict__ lse, const T* __restrict__ dO,
     float* __restrict__ dq, float* __restrict__ dws, const int* __restrict__ lens, int S, int H,
-    int Hkv, int nqt, int BH, float c, float scale) {
+    int Hkv, int nqt, int BH, int ncu, float c, float scale) {
   using C = DqCfg<T, HD>;
   using M = Mma<T>;
   __shared__ __align__(16) T sK[2][C::TILE];
@@ -65,7 +66,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     return;
   }
 
-  const int q0 = qt * C::BM + wave * 32;
+  // fp32 with four waves: the row block a wave owns follows its SIMD, block s
+  // for SIMD s in the first workgroup a CU holds (blockIdx below the CU
+  // count), block 3 - s in the second.  A causal row block further down a
+  // tile sees more keys, so each SIMD pairs a heavy block of one workgroup
+  // with a light block of the other (at S = 256: 5 + 4, 6 + 3, 7 + 2, 8 + 1
+  // key blocks).  Any placement gives a permutation of the blocks, so the
+  // results do not depend on it.  (bf16, whose blocks are a quarter as long,
+  // measured no gain.)
+  int rw = wave;
+  if constexpr (C::NW == 4 && sizeof(T) == 4) {
+    __shared__ int simd_of[C::NW];
+    const int rank = simd_rank<C::NW>(wave, lane, simd_of);
+    rw = ncu > 0 && (blockIdx.x / ncu) % 2 == 1 ? C::NW - 1 - rank : rank;
+  }
+  const int q0 = qt * C::BM + rw * 32;
   const int my_q = q0 + li;
   const bool q_ok = my_q < n;
   const bool wave_live = q0 < n;
@@ -222,14 +237,14 @@ static void dq_typed(const Dims& d, const void* q, const void* k, const void* v,
                      const float* lse, const void* dO, float* dq, float* dws, const int* lens,
                      float scale, hipStream_t stream) {
   using C = DqCfg<T, HD>;
-  static_assert(C::BM == dq_tile_rows(sizeof(T) == 4 ? 0 : 1) && C::NT <= kThreads,
+  static_assert(C::BM == dq_tile_rows(sizeof(T) == 4 ? 0 : 1, HD) && C::NT <= kThreads,
                 "tiling differs from the plan");
   const int nqt = (d.S + C::BM - 1) / C::BM;
   const int BH = d.B * d.H;
   dim3 grid((unsigned)attn_plan(d, sizeof(T) == 4 ? 0 : 1).dq_blocks), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), grid, block, 0, stream, (const T*)q,
                      (const T*)k, (const T*)v, (const T*)o, lse, (const T*)dO, dq, dws, lens, d.S,
-                     d.H, d.Hkv, nqt, BH, scale * kLog2e, scale);
+                     d.H, d.Hkv, nqt, BH, device_cu_count(), scale * kLog2e, scale);
 }
 
 void launch_bwd_dq(int dtype, const Dims& d, const void* q, const void* k, const void* v,

@@ -20,8 +20,8 @@ constexpr long long kMaxBlocks = 0xFFFFFFFFLL / kThreads;
 
 // Tiling of the attention kernels (each kernel static_asserts its own).
 constexpr int kFwdTileRows = 128;  // query rows per forward workgroup
-// query rows per dq workgroup: fp32 runs two waves, bf16 four
-constexpr int dq_tile_rows(int dtype) { return dtype == 0 ? 64 : 128; }
+// query rows per dq workgroup: four waves, except fp32 at hd 64 (two)
+constexpr int dq_tile_rows(int dtype, int hd) { return dtype == 0 && hd == 64 ? 64 : 128; }
 constexpr int kDkvTileKeys = 128;  // keys per dk/dv workgroup
 constexpr int kCmpTile = 128;      // rows and keys per composed-path tile
 

@@ -50,7 +50,7 @@ AttnPlan attn_plan(const Dims& d, int dtype, bool split_groups) {
   AttnPlan p;
   const long long BH = (long long)d.B * d.H, BG = (long long)d.B * d.Hkv;
   p.fwd_blocks = cdiv(d.S, kFwdTileRows) * BH;
-  p.dq_blocks = cdiv(d.S, dq_tile_rows(dtype)) * BH;
+  p.dq_blocks = cdiv(d.S, dq_tile_rows(dtype, d.hd)) * BH;
   p.split = split_groups ? dkdv_split(d, dtype) : 1;
   p.dkdv_blocks = cdiv(d.S, kDkvTileKeys) * BG * p.split;
   // the partial-sum kernel: 4 floats per thread over dk and dv
