@@ -1,7 +1,9 @@
 // attn_fwd.hip -- fused causal attention forward for gfx950.
 //
-// One workgroup (4 waves) per (batch, head, 128-row query tile); each wave owns
-// 32 query rows.  Key/value tiles of 64 rows are copied into a double-buffered
+// One workgroup (4 waves) per (batch, head, query tile): fp32 at hd <= 32
+// (attn_fwd_kernel) runs 64-row tiles, two waves per 32 rows, each taking one
+// 32-key block of every key tile and merged at the end; otherwise 128 rows, a
+// wave per 32 (bf16: attn_fwd_pipe_kernel, below).  Key/value tiles of 64 rows are copied into a double-buffered
 // LDS ring (bf16: asynchronously, straight from HBM into swizzled tiles; the
 // copy of tile j+1 overlaps the arithmetic on tile j; one barrier per tile) and
 // shared by the four waves.  Per tile and wave:
@@ -53,7 +55,15 @@ __device__ __forceinline__ void store_padding_rows(T* o, float* lse, int bh, int
 
 template <typename T, int HD>
 struct FwdCfg {
-  static constexpr int NW = 4, NT = NW * kWave, BM = 32 * NW, BN = 64, NB = BN / 32;
+  // hd <= 32: two row blocks of 32 queries, each split over two waves by key:
+  // wave (r, c) takes 32-key block c of every 64-key tile for rows r, keeping
+  // its own softmax state, and the two states of a row block are merged at
+  // the end.  A causal row block's serial chain of blocks is halved (at
+  // S = 256 the last rows' 8 blocks of 64-cycle fp32 products become 4 per
+  // wave).  At hd 64 the merge's registers would cost a wave per SIMD, so
+  // there each of four waves owns its 32 rows and every key.
+  static constexpr int KC = HD <= 32 ? 2 : 1, NR = 4 / KC;
+  static constexpr int NW = NR * KC, NT = NW * kWave, BM = 32 * NR, BN = 64, NB = BN / 32;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;  // head-dim contraction steps
   static constexpr int NAS = 32 / Mma<T>::KSTEP;  // key contraction steps per 32-key block
@@ -86,13 +96,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     return;
   }
 
-  const int q0 = qt * C::BM + wave * 32;
+  // row block, and key block of each tile
+  const int rw = C::KC == 1 ? wave : wave % C::NR, kc = C::KC == 1 ? 0 : wave / C::NR;
+  const int q0 = qt * C::BM + rw * 32;
   const int my_q = q0 + li;
   const bool q_ok = my_q < n;
   const bool wave_live = q0 < n;
   const int wave_kv_end = min(n, q0 + 32);  // keys visible to some row of this wave
   // padding rows of this tile are written first, while nothing is live
-  if (!q_ok && g == 0 && my_q < S) store_padding_row<T, HD>(o, lse, bh, S, my_q);
+  if (!q_ok && g == 0 && kc == 0 && my_q < S) store_padding_row<T, HD>(o, lse, bh, S, my_q);
 
   // the query operands by wide loads; a row past the sequence end reads row
   // n-1 and its operands are zeroed
@@ -135,7 +147,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
       // carry a mask (masked scores become -inf, i.e. weight exactly 0).
       bool act[C::NB];
 #pragma unroll
-      for (int cb = 0; cb < C::NB; ++cb) act[cb] = kv_t0 + 32 * cb < wave_kv_end;
+      for (int cb = 0; cb < C::NB; ++cb) act[cb] = cb % C::KC == kc && kv_t0 + 32 * cb < wave_kv_end;
       f32x16 s[C::NB];
       auto scores = [&]() {
 #pragma unroll
@@ -181,9 +193,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
       // outgrew m -- are the scores recomputed, the row max taken and the
       // accumulator rescaled.  The decision is per row (rows that pass keep m
       // and recompute the same weights), so every row's result depends only
-      // on that row's scores.  Every row fails on the first tile (key 0 is
-      // visible to all rows), so there m is the tile's row max directly, with
-      // nothing to rescale.
+      // on that row's scores.  Every row fails on the first tile (m = -inf),
+      // so there m is the tile's row max directly, with nothing to rescale; a
+      // wave whose block of that tile lies wholly above its rows sees none of
+      // the row's keys at all and keeps m = -inf, l = 0, O = 0.
       if (j == 0) {
         float mx = -INFINITY;
 #pragma unroll
@@ -233,6 +246,37 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
       stV.commit(sV[cur ^ 1], tid);
     }
     __syncthreads();
+  }
+
+  // merge the two key halves of each row block (every read of the K and V
+  // buffers ended at the last barrier): wave (r, 1) hands m, l and O to wave
+  // (r, 0), which rescales both to the larger m.  A half that saw no key of a
+  // row has m = -inf and weight exp2(-inf) = 0.
+  if constexpr (C::KC == 2) {
+    static_assert(C::NR * C::ND * 16 * kWave <= 2 * C::TILE && C::NR * 2 * kWave <= 2 * C::TILE,
+                  "partial softmax states exceed the K and V buffers");
+    float* red_o = reinterpret_cast<float*>(&sK[0][0]);
+    float* red_ml = reinterpret_cast<float*>(&sV[0][0]);
+    if (kc == 1) {
+#pragma unroll
+      for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red_o[((rw * C::ND + db) * 16 + r) * kWave + lane] = oacc[db][r];
+      red_ml[(rw * 2) * kWave + lane] = m;
+      red_ml[(rw * 2 + 1) * kWave + lane] = l;
+    }
+    __syncthreads();
+    if (kc == 1) return;
+    const float m1 = red_ml[(rw * 2) * kWave + lane], l1 = red_ml[(rw * 2 + 1) * kWave + lane];
+    const float mm = fmaxf(m, m1);
+    const float a0 = fast_exp2(m - mm), a1 = fast_exp2(m1 - mm);
+    l = l * a0 + l1 * a1;
+    m = mm;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[db][r] = oacc[db][r] * a0 + red_o[((rw * C::ND + db) * 16 + r) * kWave + lane] * a1;
   }
 
   if (!wave_live) return;  // a wave of padding rows (stored at the start)
@@ -568,7 +612,7 @@ template <typename T, int HD>
 static void fwd_typed(const Dims& d, const void* q, const void* k, const void* v, void* o,
                       float* lse, const int* lens, float scale, hipStream_t stream) {
   using C = FwdCfg<T, HD>;
-  static_assert(C::BM == kFwdTileRows && C::NT == kThreads, "tiling differs from the plan");
+  static_assert(C::BM == fwd_tile_rows(0, HD) && C::NT == kThreads, "tiling differs from the plan");
   const int nqt = (d.S + C::BM - 1) / C::BM;
   const int BH = d.B * d.H;
   dim3 grid((unsigned)attn_plan(d, 0).fwd_blocks), block(C::NT);
@@ -596,7 +640,7 @@ template <int HD>
 static void fwd_pipe(const Dims& d, const void* q, const void* k, const void* v, void* o,
                      float* lse, const int* lens, float scale, hipStream_t stream) {
   using P = FwdPipe<HD>;
-  static_assert(P::BM == kFwdTileRows && P::NT == kThreads, "tiling differs from the plan");
+  static_assert(P::BM == fwd_tile_rows(1, HD) && P::NT == kThreads, "tiling differs from the plan");
   const int nqt = (d.S + P::BM - 1) / P::BM;
   const int BH = d.B * d.H;
   dim3 grid((unsigned)attn_plan(d, 1).fwd_blocks), block(P::NT);

@@ -19,7 +19,9 @@ constexpr int kThreads = 256;
 constexpr long long kMaxBlocks = 0xFFFFFFFFLL / kThreads;
 
 // Tiling of the attention kernels (each kernel static_asserts its own).
-constexpr int kFwdTileRows = 128;  // query rows per forward workgroup
+// query rows per forward workgroup: four waves of 32 rows, except fp32 at
+// hd <= 32 (two row blocks of 32, each split over two waves by key)
+constexpr int fwd_tile_rows(int dtype, int hd) { return dtype == 0 && hd <= 32 ? 64 : 128; }
 // query rows per dq workgroup: four waves, except fp32 at hd 64 (two)
 constexpr int dq_tile_rows(int dtype, int hd) { return dtype == 0 && hd == 64 ? 64 : 128; }
 constexpr int kDkvTileKeys = 128;  // keys per dk/dv workgroup

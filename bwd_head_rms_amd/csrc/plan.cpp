@@ -49,7 +49,7 @@ size_t dkdv_part_offset(const Dims& d) {
 AttnPlan attn_plan(const Dims& d, int dtype, bool split_groups) {
   AttnPlan p;
   const long long BH = (long long)d.B * d.H, BG = (long long)d.B * d.Hkv;
-  p.fwd_blocks = cdiv(d.S, kFwdTileRows) * BH;
+  p.fwd_blocks = cdiv(d.S, fwd_tile_rows(dtype, d.hd)) * BH;
   p.dq_blocks = cdiv(d.S, dq_tile_rows(dtype, d.hd)) * BH;
   p.split = split_groups ? dkdv_split(d, dtype) : 1;
   p.dkdv_blocks = cdiv(d.S, kDkvTileKeys) * BG * p.split;
