@@ -54,8 +54,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
   using M = Mma<T>;
   __shared__ __align__(16) T sQ[2][C::TILE];
   __shared__ __align__(16) T sO[2][C::TILE];  // dO
-  __shared__ float sL[2][C::BMQ];             // LSE * log2e
-  __shared__ float sD[2][C::BMQ];
+  __shared__ __align__(16) float sL[2][C::BMQ];  // LSE * log2e (rows read four at a time)
+  __shared__ __align__(16) float sD[2][C::BMQ];
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 31, g = lane >> 5;
@@ -195,23 +195,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
       auto block = [&](const int qb, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int qb0 = qt * C::BMQ + 32 * qb;
-        f32x16 s = zero_acc(), dp = zero_acc();
+        // dP accumulates onto -D of the block's rows (the workspace holds -D)
+        // and comes out as dP - D
+        f32x16 s = zero_acc(), dp;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const float4 d4 = *reinterpret_cast<const float4*>(tD + 32 * qb + 8 * rg + 4 * g);
+          dp[4 * rg] = d4.x;
+          dp[4 * rg + 1] = d4.y;
+          dp[4 * rg + 2] = d4.z;
+          dp[4 * rg + 3] = d4.w;
+        }
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           M::mma(s, row_frag_lds<T, HD, C::BMQ>(tQ, 32 * qb + li, g, ks), kf[ks]);
           M::mma(dp, row_frag_lds<T, HD, C::BMQ>(tO, 32 * qb + li, g, ks), vf[ks]);
         }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 32 * qb + acc_row(r, g);
-          float p = fast_exp2(fmaf(s[r], c, -tL[ql]));
-          if constexpr (MASK) {
-            const int qi = qb0 + acc_row(r, g);
-            p = (qi >= my_kv && qi < n) ? p : 0.f;
+        for (int rg = 0; rg < 4; ++rg) {
+          const float4 lv = *reinterpret_cast<const float4*>(tL + 32 * qb + 8 * rg + 4 * g);
+          const float lr[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            float p = fast_exp2(fmaf(s[r], c, -lr[e]));
+            if constexpr (MASK) {
+              const int qi = qb0 + acc_row(r, g);
+              p = (qi >= my_kv && qi < n) ? p : 0.f;
+            }
+            s[r] = p;
+            dp[r] = p * dp[r];  // dS = P (dP - D)
           }
-          s[r] = p;
-          dp[r] = p * (dp[r] + tD[ql]);  // dS (the workspace holds -D)
         }
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < C::NAS; ++ks) {
           const typename M::frag pf = acc_frag<T>(s, ks * M::KPL);
@@ -222,6 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
             acc_mma(dkacc[db], accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane), sf);
           }
         }
+        __builtin_amdgcn_s_setprio(0);
       };
 
       const int qt0 = qt * C::BMQ;
