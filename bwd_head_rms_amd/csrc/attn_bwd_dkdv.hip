@@ -213,6 +213,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
           M::mma(dp, row_frag_lds<T, HD, C::BMQ>(tO, 32 * qb + li, g, ks), vf[ks]);
         }
         __builtin_amdgcn_s_setprio(0);
+        // bf16: transposed operands of both products read before the softmax
+        // gradient, so their LDS latency overlaps it (fp32's would take 32-64
+        // registers)
+        typename M::frag to[C::NAS][C::ND], tq[C::NAS][C::ND];
+        if constexpr (sizeof(T) == 2) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ks = 0; ks < C::NAS; ++ks)
+#pragma unroll
+            for (int db = 0; db < C::ND; ++db) {
+              to[ks][db] = accrow_frag<T, HD, C::BMQ>(tO, 32 * qb, ks, 32 * db, lane);
+              tq[ks][db] = accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const float4 lv = *reinterpret_cast<const float4*>(tL + 32 * qb + 8 * rg + 4 * g);
@@ -236,8 +251,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
           const typename M::frag sf = acc_frag<T>(dp, ks * M::KPL);
 #pragma unroll
           for (int db = 0; db < C::ND; ++db) {
-            acc_mma(dvacc[db], accrow_frag<T, HD, C::BMQ>(tO, 32 * qb, ks, 32 * db, lane), pf);
-            acc_mma(dkacc[db], accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane), sf);
+            if constexpr (sizeof(T) == 2) {
+              acc_mma(dvacc[db], to[ks][db], pf);
+              acc_mma(dkacc[db], tq[ks][db], sf);
+            } else {
+              acc_mma(dvacc[db], accrow_frag<T, HD, C::BMQ>(tO, 32 * qb, ks, 32 * db, lane), pf);
+              acc_mma(dkacc[db], accrow_frag<T, HD, C::BMQ>(tQ, 32 * qb, ks, 32 * db, lane), sf);
+            }
           }
         }
         __builtin_amdgcn_s_setprio(0);
