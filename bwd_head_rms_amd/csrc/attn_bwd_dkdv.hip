@@ -1,7 +1,9 @@
 // attn_bwd_dkdv.hip -- causal attention backward, key/value side, for gfx950.
 //
-// One workgroup (4 waves) per (batch, kv head, 128-row key tile); each wave owns
-// 32 key rows whose K and V operands stay in registers for the whole kernel.
+// One workgroup (4 waves) per (batch, kv head, key tile): 128 keys, a wave per
+// 32 (fp32 at hd <= 32: 64 keys, two waves per 32, each taking every other
+// query block, their sums added at the end).  A wave's K and V operands stay in
+// registers for the whole kernel.
 // The workgroup walks every query head of its GQA group (r ascending) and, for
 // each, the query tiles (128 rows for bf16, 64 for fp32) at or below the
 // diagonal (ascending), copying Q and dO (bf16: asynchronously, straight from
@@ -28,7 +30,12 @@ namespace xattn {
 
 template <typename T, int HD>
 struct DkvCfg {
-  static constexpr int NW = 4, NT = NW * kWave, BN = 32 * NW;
+  // fp32 at hd <= 32 gives each 32-key block two waves, each taking every
+  // other query block (QS = 2), and adds their sums through LDS at the end:
+  // the first key block's serial chain of 64-cycle fp32 products is halved
+  // (at S = 256 its 8 query blocks become 4 per wave)
+  static constexpr int QS = sizeof(T) == 4 && HD <= 32 ? 2 : 1;
+  static constexpr int NW = 4, NT = NW * kWave, BN = 32 * NW / QS;
   static constexpr int BMQ = sizeof(T) == 2 ? 128 : 64;  // query rows per staged tile
   static constexpr int NQB = BMQ / 32;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
@@ -94,7 +101,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
   // permutation of the blocks, so the results do not depend on it.
   __shared__ int simd_of[C::NW];
   const int rank = simd_rank<C::NW>(wave, lane, simd_of);
-  const int kb_w = ncu > 0 && (blockIdx.x / ncu) % 2 == 1 ? C::NW - 1 - rank : rank;
+  const int slot = ncu > 0 && (blockIdx.x / ncu) % 2 == 1 ? C::NW - 1 - rank : rank;
+  const int kb_w = slot / C::QS, qh = slot % C::QS;  // key block, query half
   const int kv0 = kt * C::BN + kb_w * 32;
   const int my_kv = kv0 + li;
   const bool kv_ok = my_kv < n;
@@ -357,11 +365,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
           }
         } else {
 #pragma unroll
-          for (int qb = 0; qb < C::NQB; ++qb) block(qb, std::false_type{});
+          for (int qb = 0; qb < C::NQB; ++qb)
+            if (qb % C::QS == qh) block(qb, std::false_type{});
         }
       } else {
 #pragma unroll
         for (int qb = 0; qb < C::NQB; ++qb) {
+          if (qb % C::QS != qh) continue;  // the other query half's block
           const int qb0 = qt0 + 32 * qb;
           if (qb0 + 31 < kv0 || qb0 >= n) continue;  // wholly above the diagonal, or past n
           if (qb0 < kv0 + 32 || qb0 + 32 > n)
@@ -376,6 +386,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 32 ? 
   }
 
   if constexpr (sizeof(T) == 2 && kDkvAgpr<HD>) mma_agpr_drain();
+  if constexpr (C::QS == 2) {
+    // the second query half of each key block hands its sums to the first
+    // through the Q and dO buffers (every read of them ended at the last
+    // barrier); added in that fixed order
+    static_assert(2 * C::ND * 16 * kWave <= 2 * C::TILE, "partial sums exceed the tile buffers");
+    float* red_k = reinterpret_cast<float*>(&sQ[0][0]);
+    float* red_v = reinterpret_cast<float*>(&sO[0][0]);
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          red_k[((kb_w * C::ND + db) * 16 + r) * kWave + lane] = dkacc[db][r];
+          red_v[((kb_w * C::ND + db) * 16 + r) * kWave + lane] = dvacc[db][r];
+        }
+    }
+    __syncthreads();
+    if (qh == 1) return;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dkacc[db][r] += red_k[((kb_w * C::ND + db) * 16 + r) * kWave + lane];
+        dvacc[db][r] += red_v[((kb_w * C::ND + db) * 16 + r) * kWave + lane];
+      }
+  }
   if (!kv_ok) {  // padding keys inside the sequence's last tile
     if (g == 0 && my_kv < S) {
       zero_row<HD>(outk + kvplane + (size_t)my_kv * HD);
@@ -423,7 +459,8 @@ static void dkdv_typed(const Dims& d, const void* q, const void* k, const void* 
                        const float* lse, const void* dO, float* dws, float* dk, float* dv,
                        const int* lens, float scale, bool split_groups, hipStream_t stream) {
   using C = DkvCfg<T, HD>;
-  static_assert(C::BN == kDkvTileKeys && C::NT == kThreads, "tiling differs from the plan");
+  static_assert(C::BN == dkdv_tile_keys(sizeof(T) == 4 ? 0 : 1, HD) && C::NT == kThreads,
+                "tiling differs from the plan");
   const AttnPlan p = attn_plan(d, sizeof(T) == 4 ? 0 : 1, split_groups);
   const int nkt = (d.S + C::BN - 1) / C::BN;
   const int BG = d.B * d.Hkv;

@@ -30,7 +30,7 @@ constexpr long kDkvSplitTargetF32 = 1024, kDkvSplitTargetBf16 = 512;
 
 int dkdv_split(const Dims& d, int dtype) {
   const int group = d.H / d.Hkv;
-  const long tiles = (long)d.B * d.Hkv * cdiv(d.S, kDkvTileKeys);
+  const long tiles = (long)d.B * d.Hkv * cdiv(d.S, dkdv_tile_keys(dtype, d.hd));
   if (group == 1 || tiles >= kDkvSplitBelow) return 1;
   // fewer workgroups than two per CU: split each group into the fewest slices
   // (a divisor of the group) that reach the target
@@ -52,7 +52,7 @@ AttnPlan attn_plan(const Dims& d, int dtype, bool split_groups) {
   p.fwd_blocks = cdiv(d.S, fwd_tile_rows(dtype, d.hd)) * BH;
   p.dq_blocks = cdiv(d.S, dq_tile_rows(dtype, d.hd)) * BH;
   p.split = split_groups ? dkdv_split(d, dtype) : 1;
-  p.dkdv_blocks = cdiv(d.S, kDkvTileKeys) * BG * p.split;
+  p.dkdv_blocks = cdiv(d.S, dkdv_tile_keys(dtype, d.hd)) * BG * p.split;
   // the partial-sum kernel: 4 floats per thread over dk and dv
   p.dkdv_sum_blocks = p.split > 1 ? cdiv(2 * (BG * d.S * d.hd / 4), kThreads) : 0;
   p.workspace_bytes = p.split == 1
