@@ -1,7 +1,9 @@
 // attn_bwd_dq.hip -- causal attention backward, query side, for gfx950.
 //
-// One workgroup (4 waves; fp32 at hd 64: 2) per (batch, head, query tile of 32
-// rows per wave); each wave owns 32 query rows, as in the forward.  The prologue computes
+// One workgroup per (batch, head, query tile): bf16 runs 4 waves of 32 query
+// rows (128-row tiles), as in the forward; fp32 runs 64-row tiles, two waves
+// of 32 rows at hd 64, and at hd <= 32 two waves per 32 rows, each taking half
+// of every key tile, their partial dQ added at the end.  The prologue computes
 //   D_i = sum_d dO_id * o_id
 // (the simplification of the softmax Jacobian in the fused kernel of the
 // "xtrain evolution overview", infra table row T14) and stores it for the
@@ -30,8 +32,12 @@ struct DqCfg {
   // instead of fitting four waves into 256, and runs a third faster
   // (measured: GQA fp32 workload 481 -> 314 us).  Everything else runs four,
   // one on each SIMD of the CU.
-  static constexpr int NW = sizeof(T) == 4 && HD == 64 ? 2 : 4, NT = NW * kWave, BM = 32 * NW,
-                       BN = 64, NB = BN / 32;
+  // fp32 at hd <= 32: two row blocks of 32, each split over two waves by key
+  // (KC = 2: wave (r, c) takes 32-key block c of every 64-key tile), the two
+  // partial dQ added through LDS at the end
+  static constexpr int KC = sizeof(T) == 4 && HD <= 32 ? 2 : 1;
+  static constexpr int NR = sizeof(T) == 4 ? 2 : 4;  // row blocks
+  static constexpr int NW = NR * KC, NT = NW * kWave, BM = 32 * NR, BN = 64, NB = BN / 32;
   static constexpr int ND = HD >= 32 ? HD / 32 : 1;
   static constexpr int NKS = HD / Mma<T>::KSTEP;
   static constexpr int NAS = 32 / Mma<T>::KSTEP;
@@ -66,19 +72,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     return;
   }
 
-  // fp32 with four waves: the row block a wave owns follows its SIMD, block s
-  // for SIMD s in the first workgroup a CU holds (blockIdx below the CU
-  // count), block 3 - s in the second.  A causal row block further down a
-  // tile sees more keys, so each SIMD pairs a heavy block of one workgroup
-  // with a light block of the other (at S = 256: 5 + 4, 6 + 3, 7 + 2, 8 + 1
-  // key blocks).  Any placement gives a permutation of the blocks, so the
-  // results do not depend on it.  (bf16, whose blocks are a quarter as long,
-  // measured no gain.)
-  int rw = wave;
+  // fp32 with four waves (hd <= 32: two row blocks x two key halves): the
+  // role of a wave follows its SIMD, slot s for SIMD s in the first workgroup
+  // a CU holds (blockIdx below the CU count), slot 3 - s in the second.  Slots
+  // 0-1 hold the tile's first (lighter) row block, 2-3 the second, so each
+  // SIMD pairs a heavy causal row block of one workgroup with a light one of
+  // the other.  Any placement gives a permutation of the slots, so the results
+  // do not depend on it.  (bf16, whose blocks are a quarter as long, measured
+  // no gain.)
+  int rw = wave, kc = 0;
   if constexpr (C::NW == 4 && sizeof(T) == 4) {
     __shared__ int simd_of[C::NW];
     const int rank = simd_rank<C::NW>(wave, lane, simd_of);
-    rw = ncu > 0 && (blockIdx.x / ncu) % 2 == 1 ? C::NW - 1 - rank : rank;
+    const int slot = ncu > 0 && (blockIdx.x / ncu) % 2 == 1 ? C::NW - 1 - rank : rank;
+    rw = slot / C::KC;
+    kc = slot % C::KC;
   }
   const int q0 = qt * C::BM + rw * 32;
   const int my_q = q0 + li;
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   }
   const float Drow = halves_sum(Dp);
   const float lse2 = q_ok ? lse_row * kLog2e : 0.f;
-  if (q_ok && g == 0) {
+  if (q_ok && g == 0 && kc == 0) {
     dws[(size_t)bh * S + my_q] = -Drow;  // negated: the dk/dv kernel starts dP from it
     dws[(size_t)BH * S + (size_t)bh * S + my_q] = lse2;  // for the dk/dv kernel
   }
@@ -201,6 +209,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int cb = 0; cb < C::NB; ++cb) {
         const int kb0 = kv_t0 + 32 * cb;
+        if (cb % C::KC != kc) continue;    // the other key half's block
         if (kb0 >= wave_kv_end) continue;  // wholly above this wave's rows, or past S
         if (kb0 + 31 > q0 || kb0 + 32 > n)
           block(cb, std::true_type{});
@@ -214,6 +223,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
       stV.commit(sV[cur ^ 1], tid);
     }
     __syncthreads();
+  }
+
+  if constexpr (C::KC == 2) {
+    // the second key half of each row block hands its partial dQ to the first
+    // through the K buffers (every read of them ended at the last barrier)
+    static_assert(C::NR * C::ND * 16 * kWave <= 2 * C::TILE, "partial dQ exceeds the K buffers");
+    float* red = reinterpret_cast<float*>(&sK[0][0]);
+    if (kc == 1) {
+#pragma unroll
+      for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((rw * C::ND + db) * 16 + r) * kWave + lane] = acc[db][r];
+    }
+    __syncthreads();
+    if (kc == 1) return;
+#pragma unroll
+    for (int db = 0; db < C::ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] += red[((rw * C::ND + db) * 16 + r) * kWave + lane];
   }
 
   if (!q_ok) {  // padding rows inside the sequence's last tile

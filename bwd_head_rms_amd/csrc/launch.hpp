@@ -23,7 +23,7 @@ constexpr long long kMaxBlocks = 0xFFFFFFFFLL / kThreads;
 // hd <= 32 (two row blocks of 32, each split over two waves by key)
 constexpr int fwd_tile_rows(int dtype, int hd) { return dtype == 0 && hd <= 32 ? 64 : 128; }
 // query rows per dq workgroup: four waves, except fp32 at hd 64 (two)
-constexpr int dq_tile_rows(int dtype, int hd) { return dtype == 0 && hd == 64 ? 64 : 128; }
+constexpr int dq_tile_rows(int dtype, int hd) { return dtype == 0 ? 64 : 128; }
 // keys per dk/dv workgroup: 128 (a wave per 32 keys), except fp32 at hd <= 32:
 // 64, two waves per 32 keys, each taking half of the query blocks
 constexpr int dkdv_tile_keys(int dtype, int hd) { return dtype == 0 && hd <= 32 ? 64 : 128; }
