@@ -58,9 +58,9 @@ KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "a
 # write x1.0), recorded with the sha256 of the kernel's sources at the time.
 # Reported only while the sources still match.
 MEASURED_TRAFFIC = {
-    "dkdv": {"src": "a7bf59cb82f0ded3", "read": 84.78e6, "write": 67.16e6},
-    "dq": {"src": "4f7408eacf973a1c", "read": 97.46e6, "write": 34.60e6},
-    "fwd": {"src": "1ac9b1478c3d988b", "read": 51.26e6, "write": 20.45e6},
+    "dkdv": {"src": "be9299c1c75df814", "read": 83.21e6, "write": 67.23e6},
+    "dq": {"src": "9bdfe6175be4adf4", "read": 95.51e6, "write": 34.60e6},
+    "fwd": {"src": "1ac9b1478c3d988b", "read": 50.48e6, "write": 20.45e6},
 }
 
 
