@@ -3,7 +3,8 @@
 One step = one pass of the whole path over one batch of the synthetic
 long-context workload (B4, S2048, 16 heads of 64, bf16 in / fp32 accumulate):
 xattn_fwd, then the backward as its two kernels (xattn_bwd_dq, xattn_bwd_dkdv,
-which together are exactly xattn_bwd), all through the C ABI on torch's current
+which together are exactly xattn_bwd for that shape; for short bf16 sequences,
+where xattn_bwd runs one kernel, xattn_bwd), all through the C ABI on torch's current
 stream with inputs resident in HBM.  At least W untimed warmup steps (and at
 least WARMUP_MIN_S seconds of them), then K timed steps between
 synchronisations.  HIP events around the dk/dv kernel, the longest one
@@ -15,7 +16,8 @@ kernels are timed in loops of their own after the timed region.
 Counted FLOPs (the FlashAttention-2 convention, causal half only):
     fwd 4*hd*nnz, bwd 10*hd*nnz per (batch, head), nnz = S(S+1)/2
 Per-kernel algorithmic FLOPs per (batch, head): fwd 4*hd*nnz (Q.K^T, P.V),
-dq kernel 6*hd*nnz (S, dP, dS.K), dk/dv kernel 8*hd*nnz (S, dP, P^T.dO, dS^T.Q).
+dq kernel 6*hd*nnz (S, dP, dS.K), dk/dv kernel 8*hd*nnz (S, dP, P^T.dO, dS^T.Q),
+the single backward kernel of short bf16 sequences the sum of the two (14*hd*nnz).
 
 The CPU baseline times the fp64 oracle on a bounded sample of the same
 workload (whole (batch, kv head) units) on the host's cores, rank 0, N = 1.
@@ -50,8 +52,10 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # MI355X dense MFMA
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 HBM_GBS = 8000.0
 
-KERNEL_FILES = {"fwd": "attn_fwd.hip", "dq": "attn_bwd_dq.hip", "dkdv": "attn_bwd_dkdv.hip"}
-KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "attn_bwd_dkdv_kernel"}
+KERNEL_FILES = {"fwd": "attn_fwd.hip", "dq": "attn_bwd_dq.hip", "dkdv": "attn_bwd_dkdv.hip",
+                "bwd": "attn_bwd_short.hip"}
+KERNEL_NAMES = {"fwd": "attn_fwd_kernel", "dq": "attn_bwd_dq_kernel", "dkdv": "attn_bwd_dkdv_kernel",
+                "bwd": "attn_bwd_short_kernel"}
 
 # HBM bytes per launch on the long-context workload from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (separate runs), scaled by the copy-kernel calibration (read x2.0,
@@ -224,7 +228,6 @@ def counted_flops(w):
 
 
 def run_gpu(w, steps, warmup):
-    import numpy as np
     import torch
 
     from bwd_head_rms_amd import _lib, inputs
@@ -259,7 +262,34 @@ def run_gpu(w, steps, warmup):
         _lib.check(L.xattn_bwd_dkdv(p["q"], p["k"], p["v"], p["lse"], p["dO"], p["dk"], p["dv"],
                                     *dims, p["ws"], ws_bytes, sh))
 
-    warm_steps, warm_s = warm_up(lambda: (fwd(), bwd_dq(), bwd_dkdv()), warmup)
+    def bwd_single():
+        _lib.check(L.xattn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"], p["dk"],
+                               p["dv"], *dims, p["ws"], ws_bytes, sh))
+
+    if int(L.xattn_bwd_kernel_count(w.B, w.S, w.H, w.Hkv, w.hd, code)) == 1:
+        # short bf16 sequences: xattn_bwd is one kernel (dq, dk, dv together);
+        # the events bracket it
+        return _time_steps(w, steps, warmup, dev, fwd, [], bwd_single, "bwd")
+    return _time_steps(w, steps, warmup, dev, fwd, [bwd_dq], bwd_dkdv, "dkdv",
+                       extra={"dq": bwd_dq})
+
+
+def _time_steps(w, steps, warmup, dev, fwd, before, timed, timed_name, extra=None):
+    """Warm up, then time exactly `steps` steps (fwd, the `before` calls, then
+    `timed` between two timing events); the other kernels are timed in loops
+    of their own afterwards."""
+    import numpy as np
+    import torch
+
+    sh = torch.cuda.current_stream(dev).cuda_stream
+
+    def step():
+        fwd()
+        for f in before:
+            f()
+        timed()
+
+    warm_steps, warm_s = warm_up(step, warmup)
 
     # Timed region: exactly `steps` steps.  Timing events sit only around the
     # dk/dv kernel (the roofline's kernel): every event recorded between two
@@ -273,18 +303,22 @@ def run_gpu(w, steps, warmup):
     T.record(e_start, sh)
     for i in range(steps):
         fwd()
-        bwd_dq()
+        for f in before:
+            f()
         T.record(ev[i][0], sh)
-        bwd_dkdv()
+        timed()
         T.record(ev[i][1], sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = T.ms(e_start, ev[-1][1])
-    dkdv_ms = float(np.mean([T.ms(e[0], e[1]) for e in ev]))
+    timed_ms = float(np.mean([T.ms(e[0], e[1]) for e in ev]))
     T.close()
-    # the other two kernels' durations, each timed over `steps` back-to-back
+    # the other kernels' durations, each timed over `steps` back-to-back
     # launches after the timed region (context, not part of the step's time)
-    avg = {"fwd": time_loop(fwd, steps), "dq": time_loop(bwd_dq, steps), "dkdv": dkdv_ms}
+    avg = {"fwd": time_loop(fwd, steps)}
+    for name, f in (extra or {}).items():
+        avg[name] = time_loop(f, steps)
+    avg[timed_name] = timed_ms
     return {"ms_per_step": total_ms / steps, "wall_s": wall, "kernel_ms": avg,
             "warmup_steps": warm_steps, "warmup_s": round(warm_s, 3),
             "device": torch.cuda.get_device_name(dev)}
@@ -641,8 +675,12 @@ def main():
     tflops = fl["total"] / sec / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     km = r["kernel_ms"]
-    kflops = {"fwd": fl["k_fwd"], "dq": fl["k_dq"], "dkdv": fl["k_dkdv"]}
-    dom = "dkdv"  # the longest kernel, timed by events inside the timed region
+    kflops = {"fwd": fl["k_fwd"], "dq": fl["k_dq"], "dkdv": fl["k_dkdv"],
+              "bwd": fl["k_dq"] + fl["k_dkdv"]}
+    # the backward's longest kernel, timed by events inside the timed region:
+    # dk/dv, or the single backward kernel of short bf16 sequences
+    dom = "bwd" if "bwd" in km else "dkdv"
+    bwd_ms = km["bwd"] if dom == "bwd" else km["dq"] + km["dkdv"]
     ach = kflops[dom] / (km[dom] / 1e3) / 1e12
     out = {
         "metric": METRIC,
@@ -662,9 +700,9 @@ def main():
         "pct_of_mfma_peak": round(100 * tflops / peak, 3),
         "tokens_per_s": round(w.B * w.S / sec, 1),
         "fwd_tflops": round(fl["fwd"] / (km["fwd"] / 1e3) / 1e12, 3),
-        "bwd_tflops": round(fl["bwd"] / ((km["dq"] + km["dkdv"]) / 1e3) / 1e12, 3),
+        "bwd_tflops": round(fl["bwd"] / (bwd_ms / 1e3) / 1e12, 3),
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in km.items()},
-        "kernel_timing": "dkdv: events around it in every timed step; fwd, dq: loops of K "
+        "kernel_timing": f"{dom}: events around it in every timed step; the others: loops of K "
                          "launches each, after the timed region",
         "warmup_run": {"steps": r["warmup_steps"], "seconds": r["warmup_s"],
                        "min_seconds": WARMUP_MIN_S},

@@ -13,7 +13,7 @@ SYMBOLS = ("xattn_fwd", "xattn_bwd", "xattn_bwd_workspace_bytes", "xattn_bwd_dq"
            "xattn_qknorm_rope_bwd", "xattn_decode_workspace_bytes", "xattn_decode",
            "xattn_fwd_ragged", "xattn_bwd_ragged", "xattn_composed_buffer_bytes",
            "xattn_composed_fwd", "xattn_composed_bwd", "xattn_bwd_noalloc",
-           "xattn_strerror")
+           "xattn_bwd_kernel_count", "xattn_strerror")
 
 F32, BF16 = 0, 1
 STATUS = {
@@ -48,6 +48,8 @@ def lib():
     L.xattn_bwd_workspace_bytes.restype = sz
     L.xattn_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, f, i, vp, sz, vp]
     L.xattn_bwd.restype = i
+    L.xattn_bwd_kernel_count.argtypes = [i, i, i, i, i, i]
+    L.xattn_bwd_kernel_count.restype = i
     L.xattn_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, i, f, i, vp, sz, vp]
     L.xattn_bwd_dq.restype = i
     L.xattn_bwd_dkdv.argtypes = [vp] * 7 + [i, i, i, i, i, f, i, vp, sz, vp]

@@ -16,8 +16,8 @@ LIB = os.path.join(HERE, "libxattn.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["attn_fwd.hip", "attn_bwd_dq.hip", "attn_bwd_dkdv.hip", "qknorm_rope.hip",
-           "decode_attn.hip", "composed.hip", "noalloc.hip", "plan.cpp", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd_dq.hip", "attn_bwd_dkdv.hip", "attn_bwd_short.hip",
+           "qknorm_rope.hip", "decode_attn.hip", "composed.hip", "noalloc.hip", "plan.cpp", "api.cpp"]
 
 # Packed-fp32 VALU instructions are switched off for all device code.  MFMA
 # accumulators are kept in ordinary VGPRs: the kernels post-process every score

@@ -107,6 +107,15 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   int rc = check_bwd_common(B, S, H, Hkv, hd, scale, dtype, workspace, workspace_bytes);
   if (rc != XATTN_OK) return rc;
   if (!aligned16(dk) || !aligned16(dv)) return XATTN_ERR_ALIGN;
+  const xattn::Dims d{B, S, H, Hkv, hd};
+  if (xattn::bwd_short_path(d, dtype)) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(dO) || !aligned16(dq) || !aligned16(workspace) || !aligned4(lens))
+      return XATTN_ERR_ALIGN;
+    xattn::launch_bwd_short(d, q, k, v, o, lse, dO, dq, dk, dv, lens, scale,
+                            static_cast<hipStream_t>(stream));
+    return launch_status();
+  }
   rc = bwd_dq_impl(q, k, v, o, lse, dO, lens, dq, B, S, H, Hkv, hd, scale, dtype, workspace,
                    workspace_bytes, stream);
   if (rc != XATTN_OK) return rc;
@@ -129,6 +138,14 @@ size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype
   // D and LSE*log2e per query row, plus the partial dk, dv of a group split
   // over workgroups
   return xattn::attn_plan(xattn::Dims{B, S, H, Hkv, hd}, dtype).workspace_bytes;
+}
+
+int xattn_bwd_kernel_count(int B, int S, int H, int Hkv, int hd, int dtype) {
+  if (dtype != XATTN_F32 && dtype != XATTN_BF16) return 0;
+  if (check_shape(B, S, H, Hkv, hd, dtype) != XATTN_OK) return 0;
+  const xattn::Dims d{B, S, H, Hkv, hd};
+  if (xattn::bwd_short_path(d, dtype)) return 1;
+  return xattn::attn_plan(d, dtype).split > 1 ? 3 : 2;
 }
 
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -169,9 +186,13 @@ int xattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o
   if (xattn::attn_plan(d, dtype, /*split_groups=*/false).workspace_bytes >
       xattn::kNoAllocScratchBytes)
     return XATTN_ERR_SCRATCH;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (xattn::bwd_short_path(d, dtype)) {  // needs no scratch
+    xattn::launch_bwd_short(d, q, k, v, o, lse, dO, dq, dk, dv, nullptr, scale, st);
+    return launch_status();
+  }
   float* ws = xattn::noalloc_scratch();
   if (!ws) return XATTN_ERR_HIP;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
   xattn::launch_bwd_dq(dtype, d, q, k, v, o, lse, dO, dq, ws, nullptr, scale, st);
   int s2 = launch_status();
   if (s2 != XATTN_OK) return s2;

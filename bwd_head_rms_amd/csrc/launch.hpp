@@ -64,6 +64,16 @@ void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, con
                      const float* lse, const void* dO, float* dws, float* dk, float* dv,
                      const int* lens, float scale, bool split_groups, hipStream_t stream);
 
+// Short bf16 sequences: one backward kernel per (batch, head) that holds the
+// whole head in LDS and writes dq, dk and dv (bitwise the two kernels'
+// results).  Taken for bf16, hd <= 32, S <= kShortMaxS and one query head per
+// kv head.
+constexpr int kShortMaxS = 256;
+bool bwd_short_path(const Dims& d, int dtype);
+void launch_bwd_short(const Dims& d, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dO, float* dq, float* dk, float* dv,
+                      const int* lens, float scale, hipStream_t stream);
+
 // Device address of the fixed scratch array of the allocation-free backward on
 // the current device (looked up once per device), or NULL if it cannot be
 // read.  Holds kNoAllocScratchBytes.

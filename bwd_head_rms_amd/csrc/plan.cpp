@@ -42,6 +42,10 @@ int dkdv_split(const Dims& d, int dtype) {
   return R;
 }
 
+bool bwd_short_path(const Dims& d, int dtype) {
+  return dtype == 1 && d.hd <= 32 && d.S <= kShortMaxS && d.H == d.Hkv;
+}
+
 size_t dkdv_part_offset(const Dims& d) {
   return (2 * (size_t)d.B * d.H * d.S + 3) / 4 * 4;  // floats, keeps 16-byte alignment
 }

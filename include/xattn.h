@@ -118,7 +118,10 @@ size_t xattn_bwd_workspace_bytes(int B, int S, int H, int Hkv, int hd, int dtype
  *   dq [B][H][S][hd], dk and dv [B][Hkv][S][hd] float (outputs)
  *   workspace: device scratch of at least xattn_bwd_workspace_bytes(...) bytes,
  *   16-byte aligned; its contents on entry do not matter.
- * Two kernels are enqueued in order on `stream`.
+ * Enqueues xattn_bwd_kernel_count(...) kernels in order on `stream`: for short
+ * bf16 sequences one kernel computes dq, dk and dv and leaves the workspace
+ * untouched; otherwise the dq kernel and the dk/dv kernel (plus a group-sum
+ * kernel for split GQA groups).
  * Returns an xattn_status.
  */
 int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -129,8 +132,10 @@ int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
 /*
  * The two halves of xattn_bwd, for callers that schedule them separately
  * (e.g. to overlap the query-side half with other work, or to time each).
- * xattn_bwd(...) is exactly xattn_bwd_dq(...) followed on the same stream by
- * xattn_bwd_dkdv(...) with the same arguments and workspace.
+ * xattn_bwd(...) gives bit for bit the results of xattn_bwd_dq(...) followed
+ * on the same stream by xattn_bwd_dkdv(...) with the same arguments and
+ * workspace; where xattn_bwd_kernel_count(...) is 2 or 3 it is exactly that
+ * pair of calls, where it is 1 the same arithmetic runs in one kernel.
  *
  * xattn_bwd_dq: writes dq [B][H][S][hd] float and stores, per query row,
  *   -D = -rowsum(dO * o) and LSE * log2(e) in the workspace ([2][B][H][S] float).
@@ -141,6 +146,22 @@ int xattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
  *   xattn_bwd_workspace_bytes).
  * Argument meaning, layout, validation and status codes are those of xattn_bwd.
  */
+/*
+ * Number of kernels xattn_bwd enqueues for a shape (and xattn_bwd_ragged with
+ * the same shape), 0 for an invalid one:
+ *   1  dtype bf16, hd <= 32, S <= 256 and H == Hkv: one workgroup per
+ *      (batch, head) holds the head's q, k, v and dO in LDS and computes D,
+ *      dk, dv and then dq with the dq and dk/dv kernels' arithmetic (q, k, v,
+ *      dO and o read from HBM once, one launch instead of two);
+ *   2  xattn_bwd_dq, then xattn_bwd_dkdv;
+ *   3  the same, with the dk/dv half's group sum (GQA groups split over
+ *      workgroups, see xattn_bwd_workspace_bytes).
+ * xattn_bwd_noalloc takes the same single kernel where this is 1, and the
+ * pair of kernels otherwise (it never splits groups).  Host-only; touches no
+ * device.
+ */
+int xattn_bwd_kernel_count(int B, int S, int H, int Hkv, int hd, int dtype);
+
 int xattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dO, float* dq, int B, int S, int H, int Hkv, int hd, float scale,
                  int dtype, void* workspace, size_t workspace_bytes, void* stream);

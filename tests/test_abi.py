@@ -123,6 +123,23 @@ def test_workspace_size_and_checks(L):
     assert bwd(L, H=4, Hkv=2, ws_bytes=L.xattn_bwd_workspace_bytes(1, 16, 4, 2, 16, 0) - 4) == WORKSPACE
 
 
+def test_bwd_kernel_count(L):
+    # short bf16 MHA sequences: the single-kernel backward
+    assert L.xattn_bwd_kernel_count(32, 256, 12, 12, 32, 1) == 1
+    assert L.xattn_bwd_kernel_count(1, 1, 1, 1, 16, 1) == 1
+    assert L.xattn_bwd_kernel_count(3, 100, 2, 2, 16, 1) == 1
+    # longer, fp32, hd 64 or grouped-query shapes: dq then dk/dv
+    assert L.xattn_bwd_kernel_count(32, 257, 12, 12, 32, 1) == 2
+    assert L.xattn_bwd_kernel_count(16, 256, 12, 12, 32, 0) == 2
+    assert L.xattn_bwd_kernel_count(4, 256, 4, 4, 64, 1) == 2
+    assert L.xattn_bwd_kernel_count(4, 2048, 16, 16, 64, 1) == 2
+    assert L.xattn_bwd_kernel_count(128, 256, 8, 2, 32, 1) == 2  # 512 kv tiles: no split
+    # split GQA groups add the group-sum kernel
+    assert L.xattn_bwd_kernel_count(16, 1024, 8, 2, 64, 1) == 3
+    assert L.xattn_bwd_kernel_count(1, 16, 3, 2, 16, 1) == 0  # invalid GQA shape
+    assert L.xattn_bwd_kernel_count(1, 16, 2, 2, 16, 9) == 0  # invalid dtype
+
+
 def test_size_limits(L):
     # one (batch, head) plane must stay below 2^31 elements
     assert fwd(L, S=2 ** 26, hd=64) == SHAPE

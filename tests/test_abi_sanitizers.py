@@ -47,6 +47,11 @@ void launch_bwd_dkdv(int, const Dims&, const void*, const void*, const void*, co
                      const void*, float*, float*, float*, const int*, float, bool, hipStream_t) {
   ++g_launches;
 }
+void launch_bwd_short(const Dims&, const void*, const void*, const void*, const void*,
+                      const float*, const void*, float*, float*, float*, const int*, float,
+                      hipStream_t) {
+  ++g_launches;
+}
 alignas(256) static float g_scratch_stub[64];
 float* noalloc_scratch() { return g_no_scratch ? nullptr : g_scratch_stub; }
 int device_cu_count() { return 256; }
@@ -176,11 +181,11 @@ int main() {
   EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 6, 4, 64, 0.125f, 1, ws, WS, nullptr),
          XATTN_ERR_GQA, 0);
   // fp32 dq tiles are 64 rows: 65536 * 256 * 2 dq workgroups for S = 128, too many,
-  // while the bf16 backward of the same shape fits
+  // while the bf16 backward of the same shape fits (a short sequence: one kernel)
   EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 65536, 128, 256, 256, 16, 0.25f, XATTN_F32, ws,
                    WS, nullptr), XATTN_ERR_SHAPE, 0);
   EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 32768, 128, 256, 256, 16, 0.25f, XATTN_BF16, ws,
-                   WS, nullptr), XATTN_OK, 2);
+                   WS, nullptr), XATTN_OK, 1);
   EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 65536, 128, 256, 256, 16, 0.25f, XATTN_BF16, ws,
                    WS, nullptr), XATTN_ERR_SHAPE, 0);
   g_fail = true;
@@ -194,6 +199,38 @@ int main() {
                         nullptr), XATTN_ERR_WORKSPACE, 0);
   EXPECT(xattn_bwd_dq(q, k, v, o, lse, nullptr, dq, 2, 100, 4, 2, 64, 0.125f, 1, ws, need, nullptr),
          XATTN_ERR_NULL, 0);
+
+  // --- short bf16 MHA sequences: one launch, the same checks
+  EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 4, 32, 0.125f, 1, ws, WS, nullptr),
+         XATTN_OK, 1);
+  EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 2, 256, 4, 4, 16, 0.125f, 1, ws, WS, nullptr),
+         XATTN_OK, 1);
+  EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 2, 257, 4, 4, 16, 0.125f, 1, ws, WS, nullptr),
+         XATTN_OK, 2);
+  EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 4, 32, 0.125f, 0, ws, WS, nullptr),
+         XATTN_OK, 2);
+  EXPECT(xattn_bwd(mis, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 4, 32, 0.125f, 1, ws, WS, nullptr),
+         XATTN_ERR_ALIGN, 0);
+  EXPECT(xattn_bwd(q, k, v, o, lse, dO, (float*)mis, dk, dv, 2, 100, 4, 4, 32, 0.125f, 1, ws, WS,
+                   nullptr), XATTN_ERR_ALIGN, 0);
+  EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 4, 32, 0.125f, 1, ws, 8 * 2 * 4 * 100 - 1,
+                   nullptr), XATTN_ERR_WORKSPACE, 0);
+  EXPECT(xattn_bwd_ragged(q, k, v, o, lse, dO, lens, dq, dk, dv, 2, 100, 4, 4, 32, 0.125f, 1, ws,
+                          WS, nullptr), XATTN_OK, 1);
+  EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 4, 32, 0.125f, 1, nullptr),
+         XATTN_OK, 1);
+  g_fail = true;
+  EXPECT(xattn_bwd(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 4, 32, 0.125f, 1, ws, WS, nullptr),
+         XATTN_ERR_HIP, 1);
+  {
+    const int c[] = {xattn_bwd_kernel_count(2, 100, 4, 4, 32, 1), xattn_bwd_kernel_count(2, 100, 4, 2, 64, 1),
+                     xattn_bwd_kernel_count(16, 1024, 8, 2, 64, 1), xattn_bwd_kernel_count(1, 16, 3, 2, 16, 1)};
+    if (c[0] != 1 || c[1] != 3 || c[2] != 3 || c[3] != 0) {
+      std::printf("FAIL kernel counts %d %d %d %d\n", c[0], c[1], c[2], c[3]);
+      ++g_failures;
+    }
+    g_checks += 4;
+  }
 
   // --- allocation-free backward: same checks, plus the fixed scratch's limit
   EXPECT(xattn_bwd_noalloc(q, k, v, o, lse, dO, dq, dk, dv, 2, 100, 4, 2, 64, 0.125f, 1, nullptr),
