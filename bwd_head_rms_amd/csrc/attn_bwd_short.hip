@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const bf16* __restrict__ o, const float* __restrict__ lse, const bf16* __restrict__ dO,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
-    const int* __restrict__ lens, int S, int H, float c, float scale) {
+    const int* __restrict__ lens, int S, int H, int nfull, float c, float scale) {
   using C = ShortCfg<HD>;
   using M = Mma<bf16>;
   using TL = Tile<bf16, HD, C::ROWS>;
@@ -64,7 +64,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int li = lane & 31, g = lane >> 5;
-  const int bh = blockIdx.x;
+  // workgroups below nfull take a whole head; the rest come in pairs that
+  // split one head: the first takes its key side (phase 1), the second its
+  // query side (phase 2), each computing the per-row values itself
+  int bh = blockIdx.x, role = 0;  // 0: both sides, 1: key side, 2: query side
+  if (bh >= nfull) {
+    const int x = bh - nfull;
+    bh = nfull + x / 2;
+    role = 1 + x % 2;
+  }
   const int b = bh / H;
   const size_t plane = (size_t)bh * S * HD;
   const int n = seq_len(lens, b, S);  // rows and keys past n are padding
@@ -78,9 +86,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int item = tid; item < (S - r0) * CPR; item += C::NT) {
       const size_t off = plane + (size_t)(r0 + item / CPR) * HD + 4 * (item % CPR);
-      *reinterpret_cast<float4*>(dq + off) = z;
-      *reinterpret_cast<float4*>(dk + off) = z;
-      *reinterpret_cast<float4*>(dv + off) = z;
+      if (role != 1) *reinterpret_cast<float4*>(dq + off) = z;
+      if (role != 2) {
+        *reinterpret_cast<float4*>(dk + off) = z;
+        *reinterpret_cast<float4*>(dv + off) = z;
+      }
     }
   }
   if (nb == 0) return;
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int blk = a == 0 ? blkA : blkB;
-    if (blk < 0) continue;
+    if (blk < 0 || role == 2) continue;
     const int my_kv = 32 * blk + li;
     frag kf[C::NKS], vf[C::NKS];
 #pragma unroll
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const int blk = a == 0 ? blkA : blkB;
-    if (blk < 0) continue;
+    if (blk < 0 || role == 1) continue;
     const int my_q = 32 * blk + li;
     const bool q_ok = my_q < n;
     frag qf[C::NKS], df[C::NKS];
@@ -319,10 +329,11 @@ static void short_typed(const Dims& d, const void* q, const void* k, const void*
                         const int* lens, float scale, hipStream_t stream) {
   using C = ShortCfg<HD>;
   static_assert(C::NT <= kThreads, "workgroup size differs from the plan");
-  dim3 grid((unsigned)((long long)d.B * d.H)), block(C::NT);
+  const ShortSplit sp = short_split(d, device_cu_count());
+  dim3 grid((unsigned)sp.blocks), block(C::NT);
   hipLaunchKernelGGL((attn_bwd_short_kernel<HD>), grid, block, 0, stream, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)o, lse, (const bf16*)dO, dq, dk,
-                     dv, lens, d.S, d.H, scale * kLog2e, scale);
+                     dv, lens, d.S, d.H, (int)sp.full, scale * kLog2e, scale);
 }
 
 void launch_bwd_short(const Dims& d, const void* q, const void* k, const void* v, const void* o,

@@ -70,6 +70,15 @@ void launch_bwd_dkdv(int dtype, const Dims& d, const void* q, const void* k, con
 // kv head.
 constexpr int kShortMaxS = 256;
 bool bwd_short_path(const Dims& d, int dtype);
+// Its grid: `full` workgroups of one head each, then pairs of workgroups that
+// split one head into its key side and its query side.  Two workgroups fit a
+// CU at once; with ncu CUs and B*H heads between ncu and 2*ncu, 2*ncu - B*H
+// heads are split, so that each CU holds one whole head and one half (fewer
+// heads: every head split; ncu unknown or more heads: none).
+struct ShortSplit {
+  long long full, blocks;
+};
+ShortSplit short_split(const Dims& d, int ncu);
 void launch_bwd_short(const Dims& d, const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dO, float* dq, float* dk, float* dv,
                       const int* lens, float scale, hipStream_t stream);

@@ -46,6 +46,13 @@ bool bwd_short_path(const Dims& d, int dtype) {
   return dtype == 1 && d.hd <= 32 && d.S <= kShortMaxS && d.H == d.Hkv;
 }
 
+ShortSplit short_split(const Dims& d, int ncu) {
+  const long long BH = (long long)d.B * d.H;
+  long long split = ncu > 0 ? 2LL * ncu - BH : 0;
+  split = split < 0 ? 0 : (split > BH ? BH : split);
+  return ShortSplit{BH - split, BH + split};
+}
+
 size_t dkdv_part_offset(const Dims& d) {
   return (2 * (size_t)d.B * d.H * d.S + 3) / 4 * 4;  // floats, keeps 16-byte alignment
 }

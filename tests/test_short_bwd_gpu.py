@@ -27,6 +27,10 @@ SHAPES = [  # B, S, H, hd
     (1, 255, 2, 16),
     (4, 64, 1, 32),
     (2, 200, 2, 16),
+    # 256 CUs hold two workgroups each: below 512 heads some heads are split
+    # into a key-side and a query-side workgroup (all of them below 256 heads)
+    (48, 96, 8, 32),   # 384 heads: 256 whole, 128 split
+    (64, 64, 8, 16),   # 512 heads: none split
 ]
 
 
