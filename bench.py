@@ -11,7 +11,9 @@ synchronisations.  HIP events around the dk/dv kernel, the longest one
 (timing-only events without a system-scope fence, so no cache flush separates
 the kernels), give its average duration inside the timed region, and its
 roofline is reported against MI355X's dense bf16 MFMA peak; the forward and dq
-kernels are timed in loops of their own after the timed region.
+kernels are timed in loops of their own after the timed region.  The other
+workloads (`secondary`) record no events inside their timed region, only at
+its ends, and time every kernel in loops of its own.
 
 Counted FLOPs (the FlashAttention-2 convention, causal half only):
     fwd 4*hd*nnz, bwd 10*hd*nnz per (batch, head), nnz = S(S+1)/2
@@ -227,7 +229,7 @@ def counted_flops(w):
             "k_fwd": 4 * per, "k_dq": 6 * per, "k_dkdv": 8 * per}
 
 
-def run_gpu(w, steps, warmup):
+def run_gpu(w, steps, warmup, kernel_events=True):
     import torch
 
     from bwd_head_rms_amd import _lib, inputs
@@ -269,15 +271,17 @@ def run_gpu(w, steps, warmup):
     if int(L.xattn_bwd_kernel_count(w.B, w.S, w.H, w.Hkv, w.hd, code)) == 1:
         # short bf16 sequences: xattn_bwd is one kernel (dq, dk, dv together);
         # the events bracket it
-        return _time_steps(w, steps, warmup, dev, fwd, [], bwd_single, "bwd")
-    return _time_steps(w, steps, warmup, dev, fwd, [bwd_dq], bwd_dkdv, "dkdv",
+        return _time_steps(steps, warmup, dev, fwd, [], bwd_single, "bwd", kernel_events)
+    return _time_steps(steps, warmup, dev, fwd, [bwd_dq], bwd_dkdv, "dkdv", kernel_events,
                        extra={"dq": bwd_dq})
 
 
-def _time_steps(w, steps, warmup, dev, fwd, before, timed, timed_name, extra=None):
+def _time_steps(steps, warmup, dev, fwd, before, timed, timed_name, kernel_events, extra=None):
     """Warm up, then time exactly `steps` steps (fwd, the `before` calls, then
-    `timed` between two timing events); the other kernels are timed in loops
-    of their own afterwards."""
+    `timed`).  With kernel_events, two timing events bracket `timed` in every
+    step (its duration inside the timed region, for the roofline); without,
+    events mark only the region's start and end, and `timed` is timed in a
+    loop of its own afterwards like the other kernels."""
     import numpy as np
     import torch
 
@@ -291,13 +295,14 @@ def _time_steps(w, steps, warmup, dev, fwd, before, timed, timed_name, extra=Non
 
     warm_steps, warm_s = warm_up(step, warmup)
 
-    # Timed region: exactly `steps` steps.  Timing events sit only around the
-    # dk/dv kernel (the roofline's kernel): every event recorded between two
-    # kernels lengthens the step by about a microsecond, which on the short
-    # workloads is several percent of it.
+    # Timed region: exactly `steps` steps.  Timing events sit at most around
+    # the roofline's kernel: every event recorded between two kernels
+    # lengthens the step by about a microsecond, which on the short workloads
+    # is several percent of it.
     T = TimingEvents()
     e_start = T.new()
-    ev = [[T.new() for _ in range(2)] for _ in range(steps)]
+    ev = [[T.new() for _ in range(2)] for _ in range(steps)] if kernel_events else []
+    e_end = T.new()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     T.record(e_start, sh)
@@ -305,13 +310,17 @@ def _time_steps(w, steps, warmup, dev, fwd, before, timed, timed_name, extra=Non
         fwd()
         for f in before:
             f()
-        T.record(ev[i][0], sh)
+        if kernel_events:
+            T.record(ev[i][0], sh)
         timed()
-        T.record(ev[i][1], sh)
+        if kernel_events:
+            T.record(ev[i][1], sh)
+    T.record(e_end, sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = T.ms(e_start, ev[-1][1])
-    timed_ms = float(np.mean([T.ms(e[0], e[1]) for e in ev]))
+    total_ms = T.ms(e_start, e_end)
+    timed_ms = (float(np.mean([T.ms(e[0], e[1]) for e in ev])) if kernel_events
+                else time_loop(timed, steps))
     T.close()
     # the other kernels' durations, each timed over `steps` back-to-back
     # launches after the timed region (context, not part of the step's time)
@@ -326,7 +335,7 @@ def _time_steps(w, steps, warmup, dev, fwd, before, timed, timed_name, extra=Non
 
 def run_secondary(w, steps, warmup):
     """One workload's fwd+bwd step, as the headline one is measured."""
-    r = run_gpu(w, steps, warmup)
+    r = run_gpu(w, steps, warmup, kernel_events=False)
     sec = r["ms_per_step"] / 1e3
     tf = counted_flops(w)["total"] / sec / 1e12
     return {"workload": w.name, "dtype": w.dtype, "B": w.B, "S": w.S, "H": w.H, "Hkv": w.Hkv,
