@@ -20,7 +20,9 @@
 //     load instruction;
 //   * pass 1 computes the chunk's scores into LDS and their maximum, an exp
 //     pass turns them into weights and their sum, pass 2 accumulates the
-//     weighted values -- no rescaling of running sums is ever needed;
+//     weighted values -- no rescaling of running sums is ever needed (bf16
+//     rounds the weights to bf16 for pass 2, as the forward's P.V product
+//     does, and adds two positions per v_dot2_f32_bf16);
 //   * with more than one chunk per sequence each workgroup writes its partial
 //     (unnormalised sum, max, weight sum) and a second kernel merges the chunks
 //     in ascending order.  Fixed orders throughout: results are bitwise
@@ -98,7 +100,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   // two >= kDecMinChunk) are a multiple of U
   // (4 measured best: deeper pipelines cost registers, hence resident waves)
   constexpr int U = 4 < kDecMinChunk / KPR ? 4 : kDecMinChunk / KPR;
-  __shared__ float sc[GC][kDecMaxChunk];
+  // scores, then weights, position-major: the GC heads of a position are one
+  // 4-16 byte LDS read in pass 2
+  __shared__ __align__(16) float sc[kDecMaxChunk][GC];
   __shared__ float red[kDecWaves][GC][HD];
   __shared__ float wred[kDecWaves][GC];
 
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
       for (int t = 0; t < GC; ++t) {
         const float st = live ? sv[t] : -__builtin_inff();
         mloc[t] = fmaxf(mloc[t], st);
-        if (t % TPK == piece) sc[t][jj] = st;
+        if (t % TPK == piece) sc[jj][t] = st;
       }
     }
   }
@@ -241,16 +245,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   // weights exp2(s - M) in place, and each head's weight sum
   float lsum[GC];
 #pragma unroll
-  for (int t = 0; t < GC; ++t) {
-    float a = 0.f;
-    for (int jj = tid; jj < chunk; jj += kDecThreads) {
-      const float p = fast_exp2(sc[t][jj] - M[t]);
-      sc[t][jj] = p;
-      a += p;
-    }
+  for (int t = 0; t < GC; ++t) lsum[t] = 0.f;
+  for (int jj = tid; jj < chunk; jj += kDecThreads) {
 #pragma unroll
-    for (int off = 1; off < kWave; off *= 2) a += __shfl_xor(a, off);
-    lsum[t] = a;
+    for (int t = 0; t < GC; ++t) {
+      const float p = fast_exp2(sc[jj][t] - M[t]);
+      sc[jj][t] = p;
+      lsum[t] += p;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < GC; ++t) {
+#pragma unroll
+    for (int off = 1; off < kWave; off *= 2) lsum[t] += __shfl_xor(lsum[t], off);
   }
   if (lane == 0) {
 #pragma unroll
@@ -271,22 +278,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(
   for (int t = 0; t < GC; ++t)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
-  for (int r0 = 0; r0 < rounds; r0 += U) {
+  if constexpr (sizeof(T) == 2) {
+    // bf16 takes the rounds in pairs: the two weights of a head are rounded to
+    // bf16 (as the forward rounds P before its P.V product) and each element
+    // of the two value pieces forms a bf16 pair, so one v_dot2_f32_bf16 adds
+    // both rounds' terms of an element (exact products, fp32 sum)
+    static_assert(U % 2 == 0, "rounds are taken in pairs");
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint4 zero = {0u, 0u, 0u, 0u};
+    for (int r0 = 0; r0 < rounds; r0 += U) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = r0 + u;
-      const int jj = r * KPR + wave * KPW + slot;
-      const bool live = j0 + jj < j1;
-      float vv[EPL];
-      widen<T>(buf[u], vv);
+      for (int u = 0; u < U; u += 2) {
+        const int r = r0 + u;
+        const int jj = r * KPR + wave * KPW + slot;  // round r; round r + 1 is jj + KPR
+        const bf16x8 va = __builtin_bit_cast(bf16x8, j0 + jj < j1 ? buf[u] : zero);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, j0 + jj + KPR < j1 ? buf[u + 1] : zero);
+        buf[u] = load_raw(vp + row_of(r + U < rounds ? r + U : rounds - 1));
+        buf[u + 1] = load_raw(vp + row_of(r + 1 + U < rounds ? r + 1 + U : rounds - 1));
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) vv[e] = live ? vv[e] : 0.f;
-      buf[u] = load_raw(vp + row_of(r + U < rounds ? r + U : rounds - 1));
+        for (int t = 0; t < GC; ++t) {
+          const bf16x2 pp = {(__bf16)sc[jj][t], (__bf16)sc[jj + KPR][t]};
 #pragma unroll
-      for (int t = 0; t < GC; ++t) {
-        const float p = sc[t][jj];
+          for (int e = 0; e < EPL; ++e)
+            acc[t][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{va[e], vb[e]}, acc[t][e], false);
+        }
+      }
+    }
+  } else {
+    for (int r0 = 0; r0 < rounds; r0 += U) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[t][e] += p * vv[e];
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u;
+        const int jj = r * KPR + wave * KPW + slot;
+        const bool live = j0 + jj < j1;
+        float vv[EPL];
+        widen<T>(buf[u], vv);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vv[e] = live ? vv[e] : 0.f;
+        buf[u] = load_raw(vp + row_of(r + U < rounds ? r + U : rounds - 1));
+#pragma unroll
+        for (int t = 0; t < GC; ++t) {
+          const float p = sc[jj][t];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[t][e] += p * vv[e];
+        }
       }
     }
   }
